@@ -1,0 +1,166 @@
+"""Float64 / exact-integer definitions of the method, written with numpy.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  These are the
+real-valued definitions the fp32 contract is measured against, plus brute-force
+forms used to pin the C oracle:
+
+* ``decode_codes``     : the 4-bit codes read back from the bit planes;
+* ``prefix_code`` / ``dequant``: the t-plane prefix and its mid-rise value
+  (bit-plane section of the yeyulingfeng.com write-up);
+* ``requant_direct``   : the t-bit mid-rise quantiser applied to x directly;
+* ``scores_def``       : sum_j q_hj * k_ij in float64;
+* ``plan_bruteforce``  : exhaustive integer search of sum_j w_j 4^-t_j
+  under sum_j t_j <= B (reverse water-filling section);
+* ``water_level_bisect``: the smallest theta by bisection on the fp32 bit
+  pattern, evaluated with fp32 arithmetic (an independent search for the same
+  order statistic the C oracle takes by sorting).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode_codes(planes: np.ndarray, n: int) -> np.ndarray:
+    """planes [D][4][nb] uint64 -> codes [D][n] (0..15)."""
+    D, S, nb = planes.shape
+    bits = np.arange(64, dtype=np.uint64)
+    codes = np.zeros((D, nb * 64), np.int64)
+    for s in range(4):
+        b = ((planes[:, s, :, None] >> bits[None, None, :]) & np.uint64(1)).astype(np.int64)
+        codes |= b.reshape(D, nb * 64) << (3 - s)
+    return codes[:, :n]
+
+
+def prefix_code(codes: np.ndarray, t: int) -> np.ndarray:
+    return codes >> (4 - t)
+
+
+def dequant(ct, t: int, scale) -> np.ndarray:
+    """(c_t - 2^(t-1) + 1/2) * 2^(4-t) * scale/8 in float64; 0 for t = 0."""
+    if t == 0:
+        return np.zeros(np.broadcast(ct, scale).shape)
+    delta = np.asarray(scale, np.float64) / 8.0
+    return (np.asarray(ct, np.float64) - 2.0 ** (t - 1) + 0.5) * 2.0 ** (4 - t) * delta
+
+
+def requant_direct(x, scale, t: int) -> np.ndarray:
+    """t-bit mid-rise quantiser on [-scale, scale]: cell 2^(4-t) * scale/8."""
+    cell = 2.0 ** (4 - t) * (np.asarray(scale, np.float64) / 8.0)
+    c = np.floor(np.asarray(x, np.float64) / cell) + 2 ** (t - 1)
+    return np.clip(c, 0, 2 ** t - 1).astype(np.int64)
+
+
+def pack_codes_def(keys: np.ndarray, scales_f64: np.ndarray) -> np.ndarray:
+    """codes [D][n] = clip(floor(x / (scale/8)) + 8, 0, 15) for given scales
+    [D][nb] (code 8 where the scale is 0)."""
+    keys = np.asarray(keys, np.float64)
+    n, D = keys.shape
+    blk = np.arange(n) // 64
+    sc = scales_f64[:, blk]  # [D][n]
+    delta = sc / 8.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.floor(keys.T / np.where(delta > 0, delta, 1.0)) + 8
+    c = np.clip(c, 0, 15)
+    c = np.where(delta > 0, c, 8)
+    return c.astype(np.int64)
+
+
+def dequant_keys(planes, scales, n: int, depth) -> np.ndarray:
+    """k_hat [D][n] in float64 for per-channel depths."""
+    codes = decode_codes(planes, n)
+    sc = f16_bits_to_f64(scales)[:, np.arange(n) // 64]
+    out = np.zeros(codes.shape, np.float64)
+    for j, t in enumerate(np.asarray(depth)):
+        t = int(t)
+        if t:
+            out[j] = dequant(prefix_code(codes[j], t), t, sc[j])
+    return out
+
+
+def scores_def(planes, scales, n: int, depth, q_used) -> np.ndarray:
+    """[G][n] float64: sum over channels of q_hj * k_hat_ij."""
+    kh = dequant_keys(planes, scales, n, depth)
+    return np.asarray(q_used, np.float64) @ kh
+
+
+def objective(w, t) -> float:
+    """Expected squared score error up to a constant: sum_j w_j 4^-t_j."""
+    w = np.asarray(w, np.float64)
+    return float(np.sum(w * 4.0 ** (-np.asarray(t, np.float64))))
+
+
+def plan_bruteforce(w, B: int):
+    """All depth vectors in {0..4}^D with sum <= B; returns (best objective,
+    list of all optimal depth vectors)."""
+    w = np.asarray(w, np.float64)
+    D = w.shape[0]
+    cands = [t for t in itertools.product(range(5), repeat=D) if sum(t) <= B]
+    vals = [objective(w, t) for t in cands]
+    best = min(vals)
+    return best, [t for t, v in zip(cands, vals) if v == best]
+
+
+def fp32_depths(w32: np.ndarray, theta: np.float32) -> np.ndarray:
+    """t_j = #{t < 4 : w_j > fl32(theta * 4^t)} in fp32 arithmetic."""
+    w32 = np.asarray(w32, np.float32)
+    th = np.float32(theta)
+    t = np.zeros(w32.shape, np.int64)
+    lvl = th
+    with np.errstate(over="ignore"):
+        for _ in range(4):
+            t += (w32 > lvl)
+            lvl = np.float32(lvl * np.float32(4.0))
+    return t
+
+
+def water_level_bisect(w32: np.ndarray, B: int) -> np.float32:
+    """Smallest fp32 theta >= 0 with sum_j t_j(theta) <= B, searched over the
+    monotone fp32 bit patterns 0 .. 0x7F800000."""
+    w32 = np.asarray(w32, np.float32)
+    if fp32_depths(w32, np.float32(0)).sum() <= B:
+        return np.float32(0)
+    lo, hi = 0, 0x7F800000
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        th = np.array([mid], np.uint32).view(np.float32)[0]
+        if fp32_depths(w32, th).sum() <= B:
+            hi = mid
+        else:
+            lo = mid
+    return np.array([hi], np.uint32).view(np.float32)[0]
+
+
+def water_level_log_bisect(w32: np.ndarray, B: int, steps: int = 30) -> float:
+    """The literal form: bisection on log2(theta) over the fp32 range, keeping
+    the feasible (upper) side.  Converges to within a relative 2^(-steps+~8)."""
+    w32 = np.asarray(w32, np.float64)
+    pos = w32[w32 > 0]
+    if 4 * pos.size <= B:
+        return 0.0
+    lo, hi = -160.0, 130.0
+
+    def F(lg):
+        th = 2.0 ** lg
+        return sum(int(np.sum(pos > th * 4.0 ** t)) for t in range(4))
+
+    for _ in range(steps):
+        mid = 0.5 * (lo + hi)
+        if F(mid) <= B:
+            hi = mid
+        else:
+            lo = mid
+    return 2.0 ** hi
+
+
+def topk_def(scores_row: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Brute force: full lexicographic sort by (-score, index)."""
+    s = np.asarray(scores_row[:n], np.float64)
+    s = np.where(s == 0.0, 0.0, s)
+    order = np.lexsort((np.arange(n), -s))
+    return order[:k].astype(np.int32)
