@@ -1,0 +1,160 @@
+/*
+ * fathom.h -- C ABI of the Fathom per-query variable-depth key scan for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Fathom: Per-Query Read Depth for Sparse Decoding over Offloaded KV
+ * Caches" (arXiv 2609.17652), as described on the yeyulingfeng.com write-up
+ * (sections "方法一" -- keys as bit planes, "方法二" -- reverse water-filling
+ * per query group, "基座选择" -- raw versus rotated basis) and the bit-plane
+ * figure of the paotong.dev page.  A decode step scores all n cached keys of
+ * one KV head against its G query heads from a 4-bit bit-plane index, reading
+ * only a per-channel prefix of planes, and keeps the k best keys per query
+ * head plus their union per KV head.
+ *
+ * Conventions shared by every entry point
+ *  - A "pair" is one (layer, KV head).  P pairs are processed per call; every
+ *    array below is pair-major and densely packed.
+ *  - All pointers are DEVICE pointers (hipMalloc'd, or host memory mapped
+ *    into the device address space with hipHostMalloc(..., Mapped) -- the
+ *    scan reads such an index over the host link), owned by the caller, and
+ *    16-byte aligned.  The library never allocates or frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work: they do not synchronise.  Argument checks run
+ *    on the host before anything is enqueued; a failed check enqueues nothing.
+ *  - Return value: FATHOM_OK (0) or a negative FATHOM_ERR_* code; launch
+ *    failures are reported as FATHOM_ERR_HIP.  Nothing throws.
+ *  - D (channels per head) must satisfy 1 <= D <= 128; G (query heads per KV
+ *    head) 1 <= G <= 8; n (tokens) >= 1.  nb = ceil(n / 64) blocks,
+ *    npad = 64 * nb.  Tokens n..npad-1 of the last block are padding.
+ *
+ * Index layout (per pair):
+ *    planes [D][4][nb] uint64 -- word (j, s, b): bit i is bit (3 - s) of the
+ *                                4-bit code of token 64*b + i in channel j
+ *                                (s = 0 is the sign plane).  A channel's
+ *                                t-plane prefix is t*nb contiguous words.
+ *    scales [D][nb]    uint16 -- IEEE binary16 block max |x| of (channel, block).
+ *  Footprint: 68 bytes per token per pair at D = 128.
+ */
+#ifndef FATHOM_H
+#define FATHOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FATHOM_ABI_VERSION 1
+
+#define FATHOM_OK 0
+#define FATHOM_ERR_ARG (-1)         /* null pointer, bad enum, bad budget/k  */
+#define FATHOM_ERR_SHAPE (-2)       /* P, n, D or G out of range             */
+#define FATHOM_ERR_ALIGN (-3)       /* pointer not 16-byte aligned           */
+#define FATHOM_ERR_WORKSPACE (-4)   /* workspace missing or too small        */
+#define FATHOM_ERR_UNSUPPORTED (-5) /* valid but not supported (k > 4096 ...) */
+#define FATHOM_ERR_HIP (-6)         /* a HIP launch or query failed          */
+
+#define FATHOM_DTYPE_F32 0
+#define FATHOM_DTYPE_BF16 1
+
+#define FATHOM_PLAN_WATERFILL 0 /* budget = plane bits per token (0..4D)            */
+#define FATHOM_PLAN_TOPR 1      /* budget = r channels read at 4 planes (0..D)      */
+#define FATHOM_PLAN_UNIFORM 2   /* budget = depth of every channel (0..4)           */
+
+#define FATHOM_MAX_K 4096
+
+int fathom_abi_version(void);
+const char* fathom_strerror(int status);
+
+/*
+ * fathom_pack -- quantise keys into the bit-plane index (method section one).
+ *
+ *   keys   [P][n][D]  token-major, float32 (dtype F32) or bfloat16 (BF16)
+ *   rot    [P][D][D]  or NULL.  When given, channel j of the stored key is
+ *                     sum_d rot[d][j] * key[d], evaluated as a float32 fused
+ *                     multiply-add chain over ascending d (the rotated basis
+ *                     of the basis-choice section).
+ *   planes [P][D][4][nb], scales [P][D][nb]  outputs (layout above).
+ *
+ * Per (block, channel): m = max |x| over the block's valid tokens, stored as
+ * binary16 round-to-nearest-even (saturated at 65504); cell width
+ * delta = scale / 8; code c = clamp(floor(x / delta) + 8, 0, 15) with the
+ * exact real floor; a zero scale gives code 8; padding tokens get code 8.
+ * Keys must be finite.  Errors: ERR_ARG (null, bad dtype), ERR_SHAPE, ERR_ALIGN.
+ */
+int fathom_pack(const void* keys, int32_t dtype, int32_t P, int64_t n, int32_t D,
+                const float* rot, uint64_t* planes, uint16_t* scales, void* stream);
+
+/*
+ * fathom_plan -- per-pair read plan (method section two; basis section).
+ *
+ *   q       [P][G][D] float32 query heads of each KV-head group
+ *   sigma2  [P][D]    float32 calibration variance of each stored coordinate
+ *                     (rotated-coordinate variances when keys are rotated)
+ *   rot     [P][D][D] or NULL: when given, q_used = rot^T q per head, each
+ *                     output a float32 fma chain over ascending d
+ *   budget, mode      see FATHOM_PLAN_*
+ * Outputs:
+ *   depth    [P][D] uint8   planes read per channel, 0..4
+ *   active   [P][D] int16   channels with depth > 0, ascending; rest -1
+ *   n_active [P]    int32
+ *   theta    [P]    float32 water level (0 for the fixed plans)
+ *   q_used   [P][G][D] float32 query actually scored (q, or rot^T q)
+ *
+ * WATERFILL: w_j = sigma2_j * sum_h q_used_hj^2 (float32 fma chain over
+ * ascending h, then one product; non-positive weights are 0);
+ * t_j(theta) = #{t in 0..3 : w_j > theta * 4^t}; theta = the smallest
+ * non-negative float32 with sum_j t_j(theta) <= budget (exact search over the
+ * float32 bit patterns).  TOPR: the `budget` channels of largest
+ * sum_h q_used_hj^2 (ties to the lower channel) get depth 4.  UNIFORM: every
+ * channel gets depth `budget`.
+ * Errors: ERR_ARG (null, bad mode, budget out of range), ERR_SHAPE, ERR_ALIGN.
+ */
+int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P, int32_t G,
+                int32_t D, int32_t budget, int32_t mode, uint8_t* depth, int16_t* active,
+                int32_t* n_active, float* theta, float* q_used, void* stream);
+
+/*
+ * fathom_scan -- approximate scores of every key (method section two: read
+ * the t_j-plane prefix of each active channel; limitations section: one
+ * shift-and-mask per extracted bit and G multiply-adds per element).
+ *
+ *   planes, scales       the index (may be host-mapped memory)
+ *   depth, active, n_active, q_used   a plan from fathom_plan
+ *   scores [P][G][npad]  float32 output.  Score of token i for head h:
+ *       s = 0; for each active channel j in ascending order:
+ *           s = fma(q_used[h][j], khat_ij, s)
+ *       where khat_ij = (2 c_t + 1 - 2^t) * 2^-t * scale is the exact
+ *       dequantised t_j-plane prefix c_t = c >> (4 - t_j).  Padding tokens
+ *       are -inf.
+ * Errors: ERR_ARG (null), ERR_SHAPE, ERR_ALIGN.
+ */
+int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
+                const uint8_t* depth, const int16_t* active, const int32_t* n_active,
+                const float* q_used, int32_t G, float* scores, void* stream);
+
+/*
+ * fathom_topk -- the k best keys of every query head and their union per KV
+ * head (the winner rows a step fetches).
+ *
+ *   scores    [P][G][npad] from fathom_scan
+ *   topk_idx  [P][G][k] int32 token indices ordered by (score descending,
+ *             index ascending); -0 and +0 compare equal; padding excluded
+ *   topk_val  [P][G][k] float32 their scores, or NULL
+ *   union_idx [P][G*k] int32 ascending union of the G lists, padded with -1
+ *   union_len [P] int32
+ *   ws        device workspace of at least fathom_topk_workspace_bytes()
+ * Requires 1 <= k <= min(n, FATHOM_MAX_K).  Errors: ERR_ARG, ERR_SHAPE,
+ * ERR_ALIGN, ERR_UNSUPPORTED (k > 4096), ERR_WORKSPACE.
+ */
+size_t fathom_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k);
+int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
+                int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATHOM_H */

@@ -1,0 +1,118 @@
+// C ABI entry points (declared in include/fathom.h): argument checks on the
+// host, then asynchronous launches on the caller's stream.
+#include "../../include/fathom.h"
+#include "common.h"
+
+using namespace fathom;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? FATHOM_OK : FATHOM_ERR_HIP; }
+
+inline int check_shape(int32_t P, int64_t n, int32_t D)
+{
+    if (P < 1 || n < 1 || D < 1 || D > kMaxD) return FATHOM_ERR_SHAPE;
+    if (n > ((int64_t)1 << 31) - 64) return FATHOM_ERR_SHAPE;  // token index fits int32
+    return FATHOM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fathom_abi_version(void) { return FATHOM_ABI_VERSION; }
+
+const char* fathom_strerror(int status)
+{
+    switch (status) {
+    case FATHOM_OK: return "ok";
+    case FATHOM_ERR_ARG: return "invalid argument";
+    case FATHOM_ERR_SHAPE: return "shape out of range";
+    case FATHOM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FATHOM_ERR_WORKSPACE: return "workspace missing or too small";
+    case FATHOM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FATHOM_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int fathom_pack(const void* keys, int32_t dtype, int32_t P, int64_t n, int32_t D,
+                const float* rot, uint64_t* planes, uint16_t* scales, void* stream)
+{
+    if (!keys || !planes || !scales) return FATHOM_ERR_ARG;
+    if (dtype != FATHOM_DTYPE_F32 && dtype != FATHOM_DTYPE_BF16) return FATHOM_ERR_ARG;
+    int s = check_shape(P, n, D);
+    if (s) return s;
+    if (!aligned16(keys) || !aligned16(planes) || !aligned16(scales) || (rot && !aligned16(rot)))
+        return FATHOM_ERR_ALIGN;
+    return hip_status(launch_pack(keys, dtype, P, n, D, rot, planes, scales, (hipStream_t)stream));
+}
+
+int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P, int32_t G,
+                int32_t D, int32_t budget, int32_t mode, uint8_t* depth, int16_t* active,
+                int32_t* n_active, float* theta, float* q_used, void* stream)
+{
+    if (!q || !sigma2 || !depth || !active || !n_active || !theta || !q_used) return FATHOM_ERR_ARG;
+    if (P < 1 || D < 1 || D > kMaxD || G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
+    if (mode == FATHOM_PLAN_WATERFILL) {
+        if (budget < 0 || budget > 4 * D) return FATHOM_ERR_ARG;
+    } else if (mode == FATHOM_PLAN_TOPR) {
+        if (budget < 0 || budget > D) return FATHOM_ERR_ARG;
+    } else if (mode == FATHOM_PLAN_UNIFORM) {
+        if (budget < 0 || budget > 4) return FATHOM_ERR_ARG;
+    } else {
+        return FATHOM_ERR_ARG;
+    }
+    const void* ps[] = {q, sigma2, depth, active, n_active, theta, q_used};
+    for (const void* p : ps)
+        if (!aligned16(p)) return FATHOM_ERR_ALIGN;
+    if (rot && !aligned16(rot)) return FATHOM_ERR_ALIGN;
+    return hip_status(launch_plan(q, sigma2, rot, P, G, D, budget, mode, depth, active, n_active,
+                                  theta, q_used, (hipStream_t)stream));
+}
+
+int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
+                const uint8_t* depth, const int16_t* active, const int32_t* n_active,
+                const float* q_used, int32_t G, float* scores, void* stream)
+{
+    if (!planes || !scales || !depth || !active || !n_active || !q_used || !scores)
+        return FATHOM_ERR_ARG;
+    int s = check_shape(P, n, D);
+    if (s) return s;
+    if (G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
+    const void* ps[] = {planes, scales, depth, active, n_active, q_used, scores};
+    for (const void* p : ps)
+        if (!aligned16(p)) return FATHOM_ERR_ALIGN;
+    return hip_status(launch_scan(planes, scales, P, D, n, depth, active, n_active, q_used, G,
+                                  scores, (hipStream_t)stream));
+}
+
+size_t fathom_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k)
+{
+    if (P < 1 || G < 1 || G > kMaxG || n < 1 || k < 1 || k > n || k > kMaxK) return 0;
+    return topk_layout(P, G, n, k).bytes;
+}
+
+int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
+                int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                void* ws, size_t ws_bytes, void* stream)
+{
+    if (!scores || !topk_idx || !union_idx || !union_len) return FATHOM_ERR_ARG;
+    if (P < 1 || G < 1 || G > kMaxG || n < 1) return FATHOM_ERR_SHAPE;
+    if (n > ((int64_t)1 << 31) - 64) return FATHOM_ERR_SHAPE;
+    if (k < 1 || k > n) return FATHOM_ERR_ARG;
+    if (k > kMaxK || G * k > kMaxUnion) return FATHOM_ERR_UNSUPPORTED;
+    const void* ps[] = {scores, topk_idx, union_idx, union_len};
+    for (const void* p : ps)
+        if (!aligned16(p)) return FATHOM_ERR_ALIGN;
+    if (topk_val && !aligned16(topk_val)) return FATHOM_ERR_ALIGN;
+    const TopkLayout L = topk_layout(P, G, n, k);
+    if (!ws || ws_bytes < L.bytes) return FATHOM_ERR_WORKSPACE;
+    if (!aligned16(ws)) return FATHOM_ERR_ALIGN;
+    return hip_status(launch_topk(scores, P, G, n, k, topk_idx, topk_val, union_idx, union_len, ws, L,
+                                  (hipStream_t)stream));
+}
+
+}  // extern "C"

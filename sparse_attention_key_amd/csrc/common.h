@@ -1,0 +1,122 @@
+// Internal helpers shared by the gfx950 kernels of the Fathom key scan.
+// Not part of the public ABI (that is include/fathom.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fathom {
+
+constexpr int kWave = 64;
+constexpr int kMaxD = 128;
+constexpr int kMaxG = 8;
+constexpr int kMaxK = 4096;
+constexpr int kMaxUnion = 16384;  // G * k handled by the union kernel
+
+// ---------------------------------------------------------------- numerics
+
+// IEEE binary16 -> float32 (exact), from the bit fields.
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    uint32_t ex = (h >> 10) & 31u, man = h & 1023u, sign = (h & 0x8000u) << 16;
+    uint32_t bits;
+    if (ex == 0) {
+        float v = (float)man * 5.9604644775390625e-8f;  // man * 2^-24, exact
+        return (h & 0x8000u) ? -v : v;
+    }
+    if (ex == 31) bits = sign | 0x7F800000u | (man << 13);
+    else bits = sign | ((ex + 112u) << 23) | (man << 13);
+    return __uint_as_float(bits);
+}
+
+// Non-negative finite float32 -> binary16, round to nearest even, with
+// values at or above 65520 (which would round to infinity) saturated to 65504.
+__device__ __forceinline__ uint32_t f32_to_f16_rne_sat(float m)
+{
+    uint32_t u = __float_as_uint(m) & 0x7FFFFFFFu;
+    if (u >= 0x477FF000u) return 0x7BFFu;
+    int e = (int)(u >> 23) - 127;
+    uint32_t mant = u & 0x7FFFFFu;
+    if (e >= -14) {
+        uint32_t h = ((uint32_t)(e + 15) << 10) | (mant >> 13);
+        uint32_t rem = mant & 0x1FFFu;
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;
+        return h;
+    }
+    if (e < -25) return 0u;
+    uint32_t m24 = mant | 0x800000u;
+    int sh = -1 - e;  // 14 .. 24
+    uint32_t h = m24 >> sh;
+    uint32_t rem = m24 & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (h & 1u))) h += 1u;
+    return h;
+}
+
+// Order-preserving map of a score to uint32 (ascending key = ascending
+// score); -0 is folded onto +0 so that the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float s)
+{
+    uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// Composite sort key: descending order = score descending, index ascending.
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx)
+{
+    return ((uint64_t)key << 32) | (uint64_t)(~idx);
+}
+
+// ------------------------------------------------------------ wave helpers
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ uint64_t lanes_below(int lane)
+{
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// --------------------------------------------------------- host launchers
+
+hipError_t launch_pack(const void* keys, int dtype, int P, int64_t n, int D, const float* rot,
+                       uint64_t* planes, uint16_t* scales, hipStream_t st);
+hipError_t launch_plan(const float* q, const float* sigma2, const float* rot, int P, int G, int D,
+                       int budget, int mode, uint8_t* depth, int16_t* active, int32_t* n_active,
+                       float* theta, float* q_used, hipStream_t st);
+hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,
+                       const uint8_t* depth, const int16_t* active, const int32_t* n_active,
+                       const float* q_used, int G, float* scores, hipStream_t st);
+
+struct TopkLayout {
+    int64_t m;       // selections = P * G
+    int64_t stride;  // sample every stride-th block
+    int64_t cap;     // candidate capacity per selection
+    size_t off_tau, off_count, off_cand, bytes;
+};
+TopkLayout topk_layout(int P, int G, int64_t n, int k);
+hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,
+                       float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
+                       const TopkLayout& L, hipStream_t st);
+
+}  // namespace fathom

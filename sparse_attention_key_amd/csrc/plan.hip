@@ -1,0 +1,137 @@
+// Per-pair read plan (yeyulingfeng.com write-up of Fathom, section "方法二":
+// importance = calibration variance times the group's query energy, integer
+// reverse water-filling with one water level per query group, channels at or
+// below the level skipped; section "基座选择": queries rotated into the
+// stored basis).
+//
+// One wavefront per pair; lane l owns channels l and l + 64.  The level is
+// found by bisection over the float32 bit patterns of theta (monotone for
+// theta >= 0): 31 steps, each an exact count of sum_j t_j(theta) reduced
+// across the wavefront, so the result is the exact smallest feasible level
+// with no transcendental functions involved.
+#include "common.h"
+
+namespace fathom {
+namespace {
+
+__device__ __forceinline__ int depth_at(float w, float theta)
+{
+    int t = 0;
+    float lvl = theta;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        t += (w > lvl) ? 1 : 0;
+        lvl = lvl * 4.0f;
+    }
+    return t;
+}
+
+// Sum of depths over the wavefront's channels at level theta.
+__device__ __noinline__ int total_depth(float w0, float w1, bool has0, bool has1, float theta)
+{
+    int s = (has0 ? depth_at(w0, theta) : 0) + (has1 ? depth_at(w1, theta) : 0);
+    return wave_sum_i32(s);
+}
+
+// Fixed r-channel plan: rank by group query energy, ties to the lower channel.
+__device__ int topr_depth(const float* s_sq, int D, float sq, int j, int r)
+{
+    int rank = 0;
+    for (int i = 0; i < D; ++i) rank += (s_sq[i] > sq || (s_sq[i] == sq && i < j)) ? 1 : 0;
+    return rank < r ? 4 : 0;
+}
+
+__global__ __launch_bounds__(64) void plan_kernel(const float* __restrict__ q,
+                                                  const float* __restrict__ sigma2,
+                                                  const float* __restrict__ rot, int G, int D,
+                                                  int budget, int mode,
+                                                  uint8_t* __restrict__ depth,
+                                                  int16_t* __restrict__ active,
+                                                  int32_t* __restrict__ n_active,
+                                                  float* __restrict__ theta_out,
+                                                  float* __restrict__ q_used)
+{
+    __shared__ float s_q[kMaxG][kMaxD];
+    __shared__ float s_sq[kMaxD];
+    const int p = blockIdx.x, lane = lane_id();
+    for (int e = lane; e < G * D; e += kWave) s_q[e / D][e % D] = q[(size_t)p * G * D + e];
+    __syncthreads();
+
+    float w[2] = {0.0f, 0.0f}, sq[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int j = lane + c * kWave;
+        if (j >= D) continue;
+        float acc_sq = 0.0f;
+        for (int h = 0; h < G; ++h) {
+            float qu;
+            if (rot) {
+                const float* U = rot + (size_t)p * D * D;
+                float acc = 0.0f;
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(U[(size_t)d * D + j], s_q[h][d], acc);
+                qu = acc;
+            } else {
+                qu = s_q[h][j];
+            }
+            q_used[((size_t)p * G + h) * D + j] = qu;
+            acc_sq = __builtin_fmaf(qu, qu, acc_sq);
+        }
+        sq[c] = acc_sq;
+        const float v = sigma2[(size_t)p * D + j] * acc_sq;
+        w[c] = (v > 0.0f) ? v : 0.0f;
+        s_sq[j] = acc_sq;
+    }
+    __syncthreads();
+
+    const bool has0 = lane < D, has1 = lane + kWave < D;
+    int t0 = 0, t1 = 0;
+    float theta = 0.0f;
+    if (mode == 2) {
+        t0 = budget;
+        t1 = budget;
+    } else if (mode == 1) {
+        t0 = has0 ? topr_depth(s_sq, D, sq[0], lane, budget) : 0;
+        t1 = has1 ? topr_depth(s_sq, D, sq[1], lane + kWave, budget) : 0;
+    } else {
+        if (total_depth(w[0], w[1], has0, has1, 0.0f) > budget) {
+            uint32_t lo = 0u, hi = 0x7F800000u;  // total(lo) > budget >= total(hi)
+            while (hi - lo > 1u) {
+                const uint32_t mid = lo + ((hi - lo) >> 1);
+                if (total_depth(w[0], w[1], has0, has1, __uint_as_float(mid)) <= budget) hi = mid;
+                else lo = mid;
+            }
+            theta = __uint_as_float(hi);
+        }
+        t0 = depth_at(w[0], theta);
+        t1 = depth_at(w[1], theta);
+    }
+    if (!has0) t0 = 0;
+    if (!has1) t1 = 0;
+
+    const uint64_t m0 = __ballot(t0 > 0), m1 = __ballot(t1 > 0);
+    const uint64_t below = lanes_below(lane);
+    const int na = __popcll(m0) + __popcll(m1);
+    int16_t* act = active + (size_t)p * D;
+    if (t0 > 0) act[__popcll(m0 & below)] = (int16_t)lane;
+    if (t1 > 0) act[__popcll(m0) + __popcll(m1 & below)] = (int16_t)(lane + kWave);
+    for (int e = na + lane; e < D; e += kWave) act[e] = -1;
+    if (lane < D) depth[(size_t)p * D + lane] = (uint8_t)t0;
+    if (lane + kWave < D) depth[(size_t)p * D + lane + kWave] = (uint8_t)t1;
+    if (lane == 0) {
+        n_active[p] = na;
+        theta_out[p] = theta;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const float* q, const float* sigma2, const float* rot, int P, int G, int D,
+                       int budget, int mode, uint8_t* depth, int16_t* active, int32_t* n_active,
+                       float* theta, float* q_used, hipStream_t st)
+{
+    plan_kernel<<<dim3((unsigned)P), 64, 0, st>>>(q, sigma2, rot, G, D, budget, mode, depth, active,
+                                                  n_active, theta, q_used);
+    return hipGetLastError();
+}
+
+}  // namespace fathom

@@ -1,0 +1,364 @@
+// Top-k per query head and union per KV head (yeyulingfeng.com write-up of
+// Fathom: every query head keeps the k keys of highest approximate score;
+// the group fetches the union of its G winner sets).
+//
+// Ordering: (score descending, token index ascending), -0 == +0.  Scores map
+// to order-preserving 32-bit keys and then to 64-bit composites
+// key << 32 | ~index, which are unique, so "the k largest composites" is the
+// exact answer with ties already broken.
+//
+// Pipeline per call (one selection = one (pair, head)):
+//  1. threshold: exact k-th largest composite of a SAMPLE of the tokens (every
+//     stride-th block).  Its key is a lower bound of the true k-th largest
+//     key, because the sample is a subset: every true winner passes it.
+//  2. filter:    one pass over all scores appends key >= threshold to a
+//                candidate list (wavefront-aggregated atomics).
+//  3. select:    exact k largest composites of the candidates (radix select
+//                with 11-bit digits in LDS, then an LDS bitonic sort).  A
+//                selection whose candidates overflowed their capacity runs
+//                the same select directly over all its scores instead.
+//  4. union:     LDS sort of the G*k indices of a pair, duplicates dropped.
+#include "common.h"
+
+namespace fathom {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kBins = 2048;
+constexpr int kBuf = 4096;
+
+struct SelShared {
+    uint32_t hist[kBins];
+    uint64_t buf[kBuf];
+    uint32_t wsum[kSelThreads / kWave];
+    uint32_t nbuf;
+    uint32_t bin, above, inbin;
+};
+
+struct DenseSrc {
+    const float* s;
+    int64_t n;       // valid tokens
+    int64_t stride;  // sample every stride-th block (1 = all)
+    int64_t count;   // elements enumerated
+    __device__ __forceinline__ uint64_t get(int64_t e, bool& ok) const
+    {
+        const int64_t tok = (e >> 6) * stride * 64 + (e & 63);
+        ok = tok < n;
+        const float v = ok ? s[tok] : 0.0f;
+        return composite(score_key(v), (uint32_t)tok);
+    }
+};
+
+struct CandSrc {
+    const uint64_t* c;
+    int64_t count;
+    __device__ __forceinline__ uint64_t get(int64_t e, bool& ok) const
+    {
+        ok = true;
+        return c[e];
+    }
+};
+
+// Exclusive scan of one value per thread across the workgroup.
+__device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh)
+{
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) sh.wsum[wave] = x;
+    __syncthreads();
+    uint32_t off = 0;
+    for (int w = 0; w < wave; ++w) off += sh.wsum[w];
+    __syncthreads();
+    return off + x - v;
+}
+
+// Bitonic sort of buf[0..len) descending (len a power of two, <= kBuf).
+__device__ void bitonic_desc(uint64_t* buf, int len)
+{
+    for (int k2 = 2; k2 <= len; k2 <<= 1) {
+        for (int j = k2 >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < len; i += blockDim.x) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t a = buf[i], b = buf[ixj];
+                    const bool desc = (i & k2) == 0;
+                    if (desc ? (a < b) : (a > b)) {
+                        buf[i] = b;
+                        buf[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ int pow2_ceil(int x)
+{
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+// Exact need-th largest (1-based) of the unique composites of src.
+template <class Src>
+__device__ uint64_t kth_largest(const Src& src, int need, SelShared& sh)
+{
+    uint64_t prefix = 0, pmask = 0;
+    const int shifts[6] = {53, 42, 31, 20, 9, 0};
+    for (int lvl = 0; lvl < 6; ++lvl) {
+        const int sft = shifts[lvl];
+        const uint32_t wm = (lvl == 5) ? 0x1FFu : 0x7FFu;
+        for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[i] = 0;
+        __syncthreads();
+        for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
+            bool ok;
+            const uint64_t v = src.get(e, ok);
+            if (ok && (v & pmask) == prefix) atomicAdd(&sh.hist[(uint32_t)(v >> sft) & wm], 1u);
+        }
+        __syncthreads();
+        // reversed bins 2t, 2t+1 -> bins 2047-2t, 2046-2t (top first)
+        const int t = threadIdx.x;
+        if (t == 0) {
+            sh.bin = 0;
+            sh.above = 0;
+            sh.inbin = 0;
+        }
+        const uint32_t c0 = sh.hist[kBins - 1 - 2 * t], c1 = sh.hist[kBins - 2 - 2 * t];
+        const uint32_t ex = block_excl_scan(c0 + c1, sh);
+        if (ex < (uint32_t)need && (uint32_t)need <= ex + c0) {
+            sh.bin = kBins - 1 - 2 * t;
+            sh.above = ex;
+            sh.inbin = c0;
+        } else if (ex + c0 < (uint32_t)need && (uint32_t)need <= ex + c0 + c1) {
+            sh.bin = kBins - 2 - 2 * t;
+            sh.above = ex + c0;
+            sh.inbin = c1;
+        }
+        __syncthreads();
+        const uint32_t bin = sh.bin, inbin = sh.inbin;
+        need -= (int)sh.above;
+        prefix |= (uint64_t)bin << sft;
+        pmask |= (uint64_t)wm << sft;
+        __syncthreads();
+        if (inbin <= (uint32_t)kBuf) {
+            if (threadIdx.x == 0) sh.nbuf = 0;
+            __syncthreads();
+            for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
+                bool ok;
+                const uint64_t v = src.get(e, ok);
+                if (ok && (v & pmask) == prefix) {
+                    const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
+                    if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+                }
+            }
+            __syncthreads();
+            const int len = pow2_ceil((int)inbin);
+            for (int i = (int)inbin + threadIdx.x; i < len; i += blockDim.x) sh.buf[i] = 0;
+            __syncthreads();
+            bitonic_desc(sh.buf, len);
+            const uint64_t T = sh.buf[need < 1 ? 0 : (need > kBuf ? kBuf - 1 : need - 1)];
+            __syncthreads();
+            return T;
+        }
+    }
+    return prefix;  // not reached: the last digit isolates a single composite
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt, uint32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < cnt) p[i] = v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __restrict__ scores,
+                                                                int64_t n, int64_t npad,
+                                                                int64_t stride, int64_t count,
+                                                                int64_t valid, int k,
+                                                                uint32_t* __restrict__ tau)
+{
+    __shared__ SelShared sh;
+    const int64_t m = blockIdx.x;
+    if (valid < k) {
+        if (threadIdx.x == 0) tau[m] = 0u;
+        return;
+    }
+    DenseSrc src{scores + m * npad, n, stride, count};
+    const uint64_t T = kth_largest(src, k, sh);
+    if (threadIdx.x == 0) tau[m] = (uint32_t)(T >> 32);
+}
+
+__global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ scores, int64_t n,
+                                                     int64_t npad, const uint32_t* __restrict__ tau,
+                                                     uint32_t* __restrict__ counts,
+                                                     uint64_t* __restrict__ cand, int64_t cap)
+{
+    const int64_t m = blockIdx.y;
+    const uint32_t th = tau[m];
+    const float* s = scores + m * npad;
+    const int lane = lane_id();
+    const int64_t base = (int64_t)blockIdx.x * (256 * 16);
+    for (int r = 0; r < 16; ++r) {
+        const int64_t tok = base + r * 256 + threadIdx.x;
+        bool pred = false;
+        uint32_t key = 0;
+        if (tok < n) {
+            key = score_key(s[tok]);
+            pred = key >= th;
+        }
+        const uint64_t mask = __ballot(pred);
+        if (mask == 0) continue;
+        uint32_t slot0 = 0;
+        if (lane == __ffsll((long long)mask) - 1) slot0 = atomicAdd(&counts[m], (uint32_t)__popcll(mask));
+        slot0 = __shfl(slot0, __ffsll((long long)mask) - 1, kWave);
+        if (pred) {
+            const int64_t slot = (int64_t)slot0 + __popcll(mask & lanes_below(lane));
+            if (slot < cap) cand[m * cap + slot] = composite(key, (uint32_t)tok);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ scores, int64_t n, int64_t npad, const uint32_t* __restrict__ counts,
+    const uint64_t* __restrict__ cand, int64_t cap, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_val)
+{
+    __shared__ SelShared sh;
+    const int64_t m = blockIdx.x;
+    const int64_t cnt = counts[m];
+    uint64_t T;
+    const bool dense = cnt > cap;
+    DenseSrc dsrc{scores + m * npad, n, 1, npad};
+    CandSrc csrc{cand + m * cap, cnt};
+    T = dense ? kth_largest(dsrc, k, sh) : kth_largest(csrc, k, sh);
+    // gather the k winners (composites >= T) and sort them
+    if (threadIdx.x == 0) sh.nbuf = 0;
+    __syncthreads();
+    const int64_t total = dense ? dsrc.count : csrc.count;
+    for (int64_t e = threadIdx.x; e < total; e += blockDim.x) {
+        bool ok;
+        const uint64_t v = dense ? dsrc.get(e, ok) : csrc.get(e, ok);
+        if (ok && v >= T) {
+            const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
+            if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+        }
+    }
+    __syncthreads();
+    const int len = pow2_ceil(k);
+    for (int i = k + threadIdx.x; i < len; i += blockDim.x) sh.buf[i] = 0;
+    __syncthreads();
+    bitonic_desc(sh.buf, len);
+    for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        const uint64_t v = sh.buf[i];
+        topk_idx[m * k + i] = (int32_t)(~(uint32_t)v);
+        if (topk_val) topk_val[m * k + i] = key_score((uint32_t)(v >> 32));
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __restrict__ topk_idx,
+                                                            int G, int k,
+                                                            int32_t* __restrict__ union_idx,
+                                                            int32_t* __restrict__ union_len)
+{
+    __shared__ int32_t a[kMaxUnion];
+    __shared__ uint32_t wsum[kSelThreads / kWave];
+    const int p = blockIdx.x;
+    const int total = G * k;
+    const int len = pow2_ceil(total);
+    for (int i = threadIdx.x; i < len; i += blockDim.x)
+        a[i] = i < total ? topk_idx[(size_t)p * total + i] : 0x7FFFFFFF;
+    __syncthreads();
+    for (int k2 = 2; k2 <= len; k2 <<= 1)
+        for (int j = k2 >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < len; i += blockDim.x) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const int32_t x = a[i], y = a[ixj];
+                    const bool asc = (i & k2) == 0;
+                    if (asc ? (x > y) : (x < y)) {
+                        a[i] = y;
+                        a[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    // each thread owns a contiguous run of per = len / blockDim (>= 1) slots
+    const int per = (len + blockDim.x - 1) / blockDim.x;
+    const int beg = threadIdx.x * per;
+    uint32_t cnt = 0;
+    for (int i = beg; i < beg + per && i < len; ++i)
+        cnt += (a[i] != 0x7FFFFFFF && (i == 0 || a[i] != a[i - 1])) ? 1u : 0u;
+    // exclusive scan of cnt
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t x = cnt;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    uint32_t off = 0, all = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+        if (w < wave) off += wsum[w];
+        all += wsum[w];
+    }
+    uint32_t pos = off + x - cnt;
+    int32_t* out = union_idx + (size_t)p * total;
+    for (int i = beg; i < beg + per && i < len; ++i)
+        if (a[i] != 0x7FFFFFFF && (i == 0 || a[i] != a[i - 1])) out[pos++] = a[i];
+    for (int i = (int)all + threadIdx.x; i < total; i += blockDim.x) out[i] = -1;
+    if (threadIdx.x == 0) union_len[p] = (int32_t)all;
+}
+
+}  // namespace
+
+TopkLayout topk_layout(int P, int G, int64_t n, int k)
+{
+    TopkLayout L{};
+    const int64_t nb = (n + 63) / 64;
+    L.m = (int64_t)P * G;
+    // sample stride: ~sqrt(n / 4k) blocks (power of two), so the sample and
+    // the expected candidate count (~k * stride) stay balanced
+    int64_t s = 1;
+    while ((s * 2) * (s * 2) * 4 * (int64_t)k <= n && s * 2 <= nb) s *= 2;
+    L.stride = s;
+    L.cap = 8 * (int64_t)k * s + 1024;
+    if (L.cap > nb * 64) L.cap = nb * 64;
+    L.off_tau = 0;
+    L.off_count = (size_t)L.m * 4;
+    L.off_cand = ((L.off_count + (size_t)L.m * 4) + 255) & ~(size_t)255;
+    L.bytes = L.off_cand + (size_t)L.m * (size_t)L.cap * 8;
+    return L;
+}
+
+hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,
+                       float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
+                       const TopkLayout& L, hipStream_t st)
+{
+    const int64_t nb = (n + 63) / 64, npad = nb * 64;
+    char* w = (char*)ws;
+    uint32_t* tau = (uint32_t*)(w + L.off_tau);
+    uint32_t* counts = (uint32_t*)(w + L.off_count);
+    uint64_t* cand = (uint64_t*)(w + L.off_cand);
+    const int64_t sblocks = (nb + L.stride - 1) / L.stride;
+    const int64_t last = (sblocks - 1) * L.stride;  // last sampled block
+    const int64_t valid = (sblocks - 1) * 64 + (n - last * 64 < 64 ? n - last * 64 : 64);
+
+    fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
+    threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, L.stride,
+                                                                 sblocks * 64, valid, k, tau);
+    filter_kernel<<<dim3((unsigned)((npad + 4095) / 4096), (unsigned)L.m), 256, 0, st>>>(
+        scores, n, npad, tau, counts, cand, L.cap);
+    select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
+                                                              k, topk_idx, topk_val);
+    union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(topk_idx, G, k, union_idx, union_len);
+    return hipGetLastError();
+}
+
+}  // namespace fathom

@@ -1,0 +1,172 @@
+"""Python binding of libfathom.so (the gfx950 HIP library, C ABI in
+include/fathom.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the path runs in the library's kernels.  There is no
+fallback: if the library is not built this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfathom.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fathom.h")
+
+OK = 0
+ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = -1, -2, -3, -4, -5, -6
+DTYPE_F32, DTYPE_BF16 = 0, 1
+PLAN_WATERFILL, PLAN_TOPR, PLAN_UNIFORM = 0, 1, 2
+MAX_K = 4096
+
+
+class FathomError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfathom.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FathomError("load", ERR_HIP,
+                              f"{LIB_PATH} is missing; build it with python -m sparse_attention_key_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.fathom_abi_version.argtypes, L.fathom_abi_version.restype = [], ctypes.c_int
+        L.fathom_strerror.argtypes, L.fathom_strerror.restype = [ctypes.c_int], ctypes.c_char_p
+        L.fathom_pack.argtypes = [P, i32, i32, i64, i32, P, P, P, P]
+        L.fathom_plan.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.fathom_scan.argtypes = [P, P, i32, i32, i64, P, P, P, P, i32, P, P]
+        L.fathom_topk_workspace_bytes.argtypes = [i32, i32, i64, i32]
+        L.fathom_topk_workspace_bytes.restype = sz
+        L.fathom_topk.argtypes = [P, i32, i32, i64, i32, P, P, P, P, P, sz, P]
+        for f in (L.fathom_pack, L.fathom_plan, L.fathom_scan, L.fathom_topk):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of the entry points declared in include/fathom.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(fathom_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn: str, rc: int):
+    if rc != OK:
+        raise FathomError(fn, rc, lib().fathom_strerror(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def nblocks(n: int) -> int:
+    return (n + 63) // 64
+
+
+# ------------------------------------------------------------------- pack
+
+def pack_into(keys, planes, scales, rot=None, stream=None):
+    """keys [P][n][D] float32|bfloat16 -> planes [P][D][4][nb] (int64 storage
+    of uint64 words), scales [P][D][nb] (int16 storage of fp16 bits)."""
+    P, n, D = keys.shape
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[keys.dtype]
+    _check("fathom_pack", lib().fathom_pack(_ptr(keys), dt, P, n, D, _ptr(rot), _ptr(planes),
+                                            _ptr(scales), _stream(stream)))
+
+
+def pack(keys, rot=None, stream=None):
+    P, n, D = keys.shape
+    nb = nblocks(n)
+    planes = torch.empty((P, D, 4, nb), dtype=torch.int64, device=keys.device)
+    scales = torch.empty((P, D, nb), dtype=torch.int16, device=keys.device)
+    pack_into(keys, planes, scales, rot, stream)
+    return planes, scales
+
+
+# ------------------------------------------------------------------- plan
+
+class Plan:
+    """Device buffers of a read plan for P pairs."""
+
+    def __init__(self, P: int, G: int, D: int, device="cuda"):
+        self.P, self.G, self.D = P, G, D
+        self.depth = torch.empty((P, D), dtype=torch.uint8, device=device)
+        self.active = torch.empty((P, D), dtype=torch.int16, device=device)
+        self.n_active = torch.empty((P,), dtype=torch.int32, device=device)
+        self.theta = torch.empty((P,), dtype=torch.float32, device=device)
+        self.q_used = torch.empty((P, G, D), dtype=torch.float32, device=device)
+
+
+def plan_into(plan: Plan, q, sigma2, budget: int, mode: int = PLAN_WATERFILL, rot=None, stream=None):
+    P, G, D = q.shape
+    _check("fathom_plan", lib().fathom_plan(
+        _ptr(q), _ptr(sigma2), _ptr(rot), P, G, D, int(budget), int(mode), _ptr(plan.depth),
+        _ptr(plan.active), _ptr(plan.n_active), _ptr(plan.theta), _ptr(plan.q_used), _stream(stream)))
+    return plan
+
+
+def plan(q, sigma2, budget: int, mode: int = PLAN_WATERFILL, rot=None, stream=None) -> Plan:
+    P, G, D = q.shape
+    return plan_into(Plan(P, G, D, q.device), q, sigma2, budget, mode, rot, stream)
+
+
+# ------------------------------------------------------------------- scan
+
+def scan_into(planes, scales, n: int, pl: Plan, scores, stream=None):
+    P, D = pl.P, pl.D
+    _check("fathom_scan", lib().fathom_scan(
+        _ptr(planes), _ptr(scales), P, D, int(n), _ptr(pl.depth), _ptr(pl.active), _ptr(pl.n_active),
+        _ptr(pl.q_used), pl.G, _ptr(scores), _stream(stream)))
+
+
+def scan(planes, scales, n: int, pl: Plan, stream=None):
+    scores = torch.empty((pl.P, pl.G, nblocks(n) * 64), dtype=torch.float32, device=pl.q_used.device)
+    scan_into(planes, scales, n, pl, scores, stream)
+    return scores
+
+
+# ------------------------------------------------------------------ top-k
+
+def topk_workspace_bytes(P: int, G: int, n: int, k: int) -> int:
+    return int(lib().fathom_topk_workspace_bytes(P, G, int(n), int(k)))
+
+
+class TopkOut:
+    def __init__(self, P: int, G: int, n: int, k: int, device="cuda", with_values=True):
+        self.P, self.G, self.n, self.k = P, G, n, k
+        self.idx = torch.empty((P, G, k), dtype=torch.int32, device=device)
+        self.val = torch.empty((P, G, k), dtype=torch.float32, device=device) if with_values else None
+        self.union = torch.empty((P, G * k), dtype=torch.int32, device=device)
+        self.union_len = torch.empty((P,), dtype=torch.int32, device=device)
+        nbytes = max(topk_workspace_bytes(P, G, n, k), 16)
+        self.ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def topk_into(scores, n: int, out: TopkOut, stream=None):
+    P, G, _ = scores.shape
+    _check("fathom_topk", lib().fathom_topk(
+        _ptr(scores), P, G, int(n), out.k, _ptr(out.idx), _ptr(out.val), _ptr(out.union),
+        _ptr(out.union_len), _ptr(out.ws), out.ws.numel(), _stream(stream)))
+    return out
+
+
+def topk(scores, n: int, k: int, stream=None) -> TopkOut:
+    P, G, _ = scores.shape
+    return topk_into(scores, n, TopkOut(P, G, n, k, scores.device), stream)

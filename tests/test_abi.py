@@ -1,0 +1,97 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point,
+and rejects bad arguments on the host before touching HIP."""
+import ctypes
+
+import pytest
+
+from sparse_attention_key_amd import fathom as F
+
+
+@pytest.fixture(scope="module")
+def L():
+    return F.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = F.declared_symbols()
+    assert {"fathom_pack", "fathom_plan", "fathom_scan", "fathom_topk"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror(L):
+    assert L.fathom_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.fathom_strerror(code)
+    assert L.fathom_strerror(-99) == b"unknown status"
+
+
+A = ctypes.c_void_p(16 * 4096)      # aligned dummy (never dereferenced)
+MIS = ctypes.c_void_p(16 * 4096 + 4)  # misaligned dummy
+
+
+def test_pack_validation(L):
+    assert L.fathom_pack(None, 0, 1, 64, 128, None, A, A, None) == F.ERR_ARG
+    assert L.fathom_pack(A, 7, 1, 64, 128, None, A, A, None) == F.ERR_ARG
+    assert L.fathom_pack(A, 0, 0, 64, 128, None, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_pack(A, 0, 1, 0, 128, None, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_pack(A, 0, 1, 64, 129, None, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_pack(A, 0, 1, 1 << 31, 128, None, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_pack(MIS, 0, 1, 64, 128, None, A, A, None) == F.ERR_ALIGN
+    assert L.fathom_pack(A, 1, 1, 64, 128, MIS, A, A, None) == F.ERR_ALIGN
+
+
+def test_plan_validation(L):
+    args = lambda **kw: [kw.get("q", A), A, kw.get("rot", None), kw.get("P", 1), kw.get("G", 4),
+                         kw.get("D", 128), kw.get("B", 48), kw.get("mode", 0), A, A, A, A, A, None]
+    assert L.fathom_plan(*args(q=None)) == F.ERR_ARG
+    assert L.fathom_plan(*args(G=9)) == F.ERR_SHAPE
+    assert L.fathom_plan(*args(G=0)) == F.ERR_SHAPE
+    assert L.fathom_plan(*args(D=0)) == F.ERR_SHAPE
+    assert L.fathom_plan(*args(B=-1)) == F.ERR_ARG
+    assert L.fathom_plan(*args(B=513)) == F.ERR_ARG
+    assert L.fathom_plan(*args(B=129, mode=1)) == F.ERR_ARG
+    assert L.fathom_plan(*args(B=5, mode=2)) == F.ERR_ARG
+    assert L.fathom_plan(*args(mode=3)) == F.ERR_ARG
+    assert L.fathom_plan(*args(q=MIS)) == F.ERR_ALIGN
+    assert L.fathom_plan(*args(rot=MIS)) == F.ERR_ALIGN
+
+
+def test_scan_validation(L):
+    base = [A, A, 1, 128, 4096, A, A, A, A, 4, A, None]
+    bad = list(base)
+    bad[10] = None
+    assert L.fathom_scan(*bad) == F.ERR_ARG
+    bad = list(base)
+    bad[9] = 9
+    assert L.fathom_scan(*bad) == F.ERR_SHAPE
+    bad = list(base)
+    bad[4] = 0
+    assert L.fathom_scan(*bad) == F.ERR_SHAPE
+    bad = list(base)
+    bad[0] = MIS
+    assert L.fathom_scan(*bad) == F.ERR_ALIGN
+
+
+def test_topk_validation(L):
+    ws = L.fathom_topk_workspace_bytes(2, 4, 4096, 64)
+    assert ws > 0
+    assert L.fathom_topk_workspace_bytes(2, 4, 4096, 5000) == 0
+    ok = lambda **kw: [kw.get("s", A), 2, kw.get("G", 4), kw.get("n", 4096), kw.get("k", 64), A, None,
+                       A, A, kw.get("ws", A), kw.get("wsb", ws), None]
+    assert L.fathom_topk(*ok(s=None)) == F.ERR_ARG
+    assert L.fathom_topk(*ok(k=0)) == F.ERR_ARG
+    assert L.fathom_topk(*ok(k=4097, n=10000)) == F.ERR_UNSUPPORTED
+    assert L.fathom_topk(*ok(G=8, k=4096)) == F.ERR_UNSUPPORTED
+    assert L.fathom_topk(*ok(k=5000)) == F.ERR_ARG
+    assert L.fathom_topk(*ok(wsb=ws - 1)) == F.ERR_WORKSPACE
+    assert L.fathom_topk(*ok(ws=None)) == F.ERR_WORKSPACE
+    assert L.fathom_topk(*ok(s=MIS)) == F.ERR_ALIGN
+    assert L.fathom_topk(*ok(G=0)) == F.ERR_SHAPE
+
+
+def test_workspace_scales_with_sample_stride(L):
+    # 1M tokens, 288 pairs x 4 heads, k = 512: candidate lists stay well below
+    # the 4.8 GB a full score copy would need
+    b = L.fathom_topk_workspace_bytes(288, 4, 1 << 20, 512)
+    assert 0 < b < 1 << 30

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bit-exact: pack (planes, scales), plan (depths, level, active list, q_used),
+fp32 scores, top-k indices and values, union.  Scores are also checked against
+the float64 definition: |s - s_def| <= 1e-5 |s_def| + 1e-6 ||q_h||_1 max scale.
+Inputs all come from the seeded generators in workloads/ or numpy.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.gpu_util import bf16_dev, dev, need_gpu, say, score_tol, u16, u64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    need_gpu()
+    from sparse_attention_key_amd import fathom
+
+    fathom.lib()
+    return fathom
+
+
+def _np_keys(case):
+    g = np.random.default_rng(zlib.crc32(case.encode()))
+    if case == "tiny_f32":
+        return wl.keys_host(wl.WORKLOADS["tiny"], 0), "f32"
+    if case == "ragged_bf16":
+        return wl.keys_host(wl.WORKLOADS["qwen32k"], 3, n=4096 + 37), "bf16"
+    if case == "n1":
+        return g.standard_normal((1, 128)).astype(np.float32), "f32"
+    if case == "n63":
+        return g.standard_normal((63, 128)).astype(np.float32), "f32"
+    if case == "n65_bf16":
+        return wl.to_bf16_exact(g.standard_normal((65, 128)).astype(np.float32) * 7), "bf16"
+    if case == "d64":
+        return g.standard_normal((1000, 64)).astype(np.float32), "f32"
+    if case == "d96":
+        return g.standard_normal((777, 96)).astype(np.float32), "f32"
+    if case == "boundaries":
+        x = g.standard_normal((64 * 6, 128)).astype(np.float32)
+        sc = np.abs(x).reshape(6, 64, 128).max(1).astype(np.float16).astype(np.float32)
+        cells = g.integers(-8, 8, x.shape).astype(np.float32)
+        x = (cells * np.repeat(sc, 64, 0) / np.float32(8)).astype(np.float32)
+        x[::64] = np.repeat(sc, 1, 0)  # put the max back in every block
+        x[1::64] = -np.repeat(sc, 1, 0)
+        x[:, :16] = np.nextafter(x[:, :16], np.float32(np.inf))
+        x[:, 16:32] = np.nextafter(x[:, 16:32], np.float32(-np.inf))
+        x[:, 32:40] = 0.0
+        x[:, 40:48] *= np.float32(1e-6)
+        x[:64, 48] = np.float32(70000.0)  # saturating scale
+        return x, "f32"
+    raise KeyError(case)
+
+
+PACK_CASES = ["tiny_f32", "ragged_bf16", "n1", "n63", "n65_bf16", "d64", "d96", "boundaries"]
+
+
+@pytest.mark.parametrize("case", PACK_CASES)
+def test_pack_bit_exact(F, orc, case):
+    x, dt = _np_keys(case)
+    say("pack", case, x.shape, dt)
+    keys = (bf16_dev(x) if dt == "bf16" else dev(x))[None]
+    planes, scales = F.pack(keys)
+    rp, rs = orc.pack(x)
+    assert np.array_equal(u16(scales)[0], rs)
+    assert np.array_equal(u64(planes)[0], rp)
+
+
+def test_pack_multi_pair_and_rotation(F, orc):
+    g = np.random.default_rng(7)
+    xs = [g.standard_normal((300, 128)).astype(np.float32) * np.exp(g.standard_normal(128)).astype(np.float32)
+          for _ in range(3)]
+    rots = [orc.calib.klt_basis(g.standard_normal((2000, 128)) @ g.standard_normal((128, 128)))[0]
+            for _ in range(3)]
+    say("pack multi-pair + rotation")
+    keys = dev(np.stack(xs))
+    planes, scales = F.pack(keys)
+    planes_r, scales_r = F.pack(keys, rot=dev(np.stack(rots)))
+    for p in range(3):
+        rp, rs = orc.pack(xs[p])
+        assert np.array_equal(u64(planes)[p], rp) and np.array_equal(u16(scales)[p], rs)
+        rp, rs = orc.pack(xs[p], rot=rots[p])
+        assert np.array_equal(u64(planes_r)[p], rp) and np.array_equal(u16(scales_r)[p], rs)
+
+
+def _plan_inputs(P, G, D, seed):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((P, G, D)).astype(np.float32)
+    q *= np.exp(g.standard_normal((P, 1, D)) * 1.5).astype(np.float32)
+    s2 = np.exp(g.standard_normal((P, D)) * 2).astype(np.float32)
+    s2[0, :3] = 0.0
+    if P > 2:
+        s2[1] = s2[1, 0]  # all weights driven by q only
+        q[2, :, :D // 2] = q[2, :, D - D // 2:]  # repeated weights (ties at the level)
+    return q, s2
+
+
+PLAN_CASES = [(0, b) for b in (0, 1, 7, 32, 48, 68, 92, 136, 300, 511, 512)] + \
+             [(1, r) for r in (0, 16, 32, 128)] + [(2, d) for d in (0, 1, 2, 4)]
+
+
+@pytest.mark.parametrize("mode,budget", PLAN_CASES)
+def test_plan_bit_exact(F, orc, mode, budget):
+    P, G, D = 12, 4, 128
+    q, s2 = _plan_inputs(P, G, D, 100 + budget)
+    say("plan", mode, budget)
+    pl = F.plan(dev(q), dev(s2), budget, mode)
+    depth = pl.depth.cpu().numpy()
+    act = pl.active.cpu().numpy()
+    na = pl.n_active.cpu().numpy()
+    th = pl.theta.cpu().numpy()
+    qu = pl.q_used.cpu().numpy()
+    for p in range(P):
+        rd, rth, rq = orc.plan(q[p], s2[p], budget, mode)
+        assert np.array_equal(depth[p], rd), p
+        assert th[p].view(np.uint32) == np.float32(rth).view(np.uint32)
+        assert np.array_equal(qu[p].view(np.uint32), rq.view(np.uint32))
+        nz = np.nonzero(rd)[0]
+        assert na[p] == nz.size
+        assert np.array_equal(act[p, :nz.size], nz) and np.all(act[p, nz.size:] == -1)
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 128), (8, 64), (3, 96)])
+def test_plan_rotated_and_shapes(F, orc, G, D):
+    P = 5
+    q, s2 = _plan_inputs(P, G, D, 7 * G + D)
+    g = np.random.default_rng(G * D)
+    rot = np.stack([np.linalg.qr(g.standard_normal((D, D)))[0] for _ in range(P)]).astype(np.float32)
+    say("plan rotated", G, D)
+    pl = F.plan(dev(q), dev(s2), 48, 0, rot=dev(rot))
+    for p in range(P):
+        rd, rth, rq = orc.plan(q[p], s2[p], 48, 0, rot=rot[p])
+        assert np.array_equal(pl.depth.cpu().numpy()[p], rd)
+        assert np.array_equal(pl.q_used.cpu().numpy()[p].view(np.uint32), rq.view(np.uint32))
+
+
+SCAN_CASES = [  # (n, D, G, mode, budget)
+    (4096, 128, 4, 0, 48), (4096 + 37, 128, 4, 0, 48), (1, 128, 4, 0, 48), (700, 128, 4, 0, 512),
+    (700, 128, 4, 0, 0), (2000, 128, 4, 1, 32), (2000, 128, 4, 2, 2), (1500, 64, 8, 0, 92),
+    (999, 96, 1, 0, 136), (3333, 128, 7, 0, 17),
+]
+
+
+@pytest.mark.parametrize("n,D,G,mode,budget", SCAN_CASES)
+def test_scan_bit_exact_and_within_tolerance(F, orc, n, D, G, mode, budget):
+    P = 2
+    g = np.random.default_rng(n + D + G + budget)
+    x = [(g.standard_normal((n, D)) * np.exp(g.standard_normal(D))).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, n)
+    say("scan", n, D, G, mode, budget)
+    planes, scales = F.pack(dev(np.stack(x)))
+    pl = F.plan(dev(q), dev(s2), budget, mode)
+    scores = F.scan(planes, scales, n, pl).cpu().numpy()
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        rd, _, rq = orc.plan(q[p], s2[p], budget, mode)
+        ref = orc.scores_f32(rp, rs, n, rd, rq)
+        assert np.array_equal(scores[p].view(np.uint32), ref.view(np.uint32))
+        d64 = orc.ref64.scores_def(rp, rs, n, rd, rq)
+        assert np.all(np.abs(scores[p][:, :n] - d64) <= score_tol(d64, rq, rs))
+
+
+def _topk_check(F, orc, s, n, k):
+    P, G, _ = s.shape
+    out = F.topk(dev(s), n, k)
+    idx = out.idx.cpu().numpy()
+    val = out.val.cpu().numpy()
+    un = out.union.cpu().numpy()
+    ul = out.union_len.cpu().numpy()
+    for p in range(P):
+        refs = []
+        for h in range(G):
+            ri, rv = orc.topk(s[p, h], n, k)
+            assert np.array_equal(idx[p, h], ri), (p, h)
+            assert np.array_equal(val[p, h], rv)
+            refs.append(ri)
+        ru, rl = orc.union(np.stack(refs))
+        assert ul[p] == rl and np.array_equal(un[p], ru)
+
+
+TOPK_CASES = [  # (n, k, kind)
+    (4096, 64, "normal"), (32768, 512, "normal"), (100000, 512, "ties"), (70, 70, "normal"),
+    (1, 1, "normal"), (64 * 33 + 5, 200, "ties"), (20000, 4096, "normal"), (5000, 1, "ties"),
+    (200000, 512, "allequal"), (131072, 2048, "normal"),
+]
+
+
+@pytest.mark.parametrize("n,k,kind", TOPK_CASES)
+def test_topk_union_bit_exact(F, orc, n, k, kind):
+    P, G = 2, 4
+    npad = (n + 63) // 64 * 64
+    g = np.random.default_rng(n + k)
+    s = g.standard_normal((P, G, npad)).astype(np.float32)
+    if kind == "ties":
+        s = np.round(s * 3).astype(np.float32)
+        s[..., ::5] = -0.0
+    if kind == "allequal":  # every score tied: candidates overflow -> dense path
+        s[:] = 1.5
+    s[..., n:] = -np.inf
+    say("topk", n, k, kind)
+    _topk_check(F, orc, s, n, k)
+
+
+def _run_pipeline(F, planes, scales, n, q, s2, budget, k, mode=0, rot=None):
+    pl = F.plan(q, s2, budget, mode, rot=rot)
+    scores = F.scan(planes, scales, n, pl)
+    out = F.topk(scores, n, k)
+    return pl, scores, out
+
+
+def _compare_pair(orc, p, x, q, s2, budget, k, n, pl, scores, out, mode=0, rot=None, keys_rot=None):
+    rp, rs = orc.pack(x, rot=keys_rot)
+    ref = orc.step(rp, rs, n, q, s2, budget, k, mode=mode, rot=rot)
+    assert np.array_equal(pl.depth[p].cpu().numpy(), ref["depth"])
+    assert np.array_equal(scores[p].cpu().numpy().view(np.uint32), ref["scores"].view(np.uint32))
+    assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"])
+    assert out.union_len[p].item() == ref["union_len"]
+    assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+    return rp, rs
+
+
+def test_end_to_end_tiny(F, orc):
+    w = wl.WORKLOADS["tiny"]
+    x = wl.keys_host(w, 0)
+    q = wl.queries(w, 0)
+    s2 = orc.calib.channel_variance(wl.calibration_sample(w, 0))
+    say("end-to-end tiny")
+    planes, scales = F.pack(dev(x)[None])
+    pl, scores, out = _run_pipeline(F, planes, scales, w.n, dev(q)[None], dev(s2)[None], w.budget, w.k)
+    _compare_pair(orc, 0, x, q, s2, w.budget, w.k, w.n, pl, scores, out)
+    pos = wl.planted_positions(w, 0)
+    for h in range(w.G):
+        assert set(pos[h]) <= set(out.idx[0, h].cpu().numpy())
+
+
+def test_end_to_end_qwen32k(F, orc):
+    w = wl.WORKLOADS["qwen32k"]
+    xs = [wl.keys_host(w, p) for p in range(w.P)]
+    qs = np.stack([wl.queries(w, p) for p in range(w.P)])
+    s2 = np.stack([orc.calib.channel_variance(wl.calibration_sample(w, p)) for p in range(w.P)])
+    say("end-to-end qwen32k")
+    planes, scales = F.pack(bf16_dev(np.stack(xs)))
+    pl, scores, out = _run_pipeline(F, planes, scales, w.n, dev(qs), dev(s2), w.budget, w.k)
+    for p in range(w.P):
+        _compare_pair(orc, p, xs[p], qs[p], s2[p], w.budget, w.k, w.n, pl, scores, out)
+
+
+def test_end_to_end_rotated_small(F, orc):
+    w = wl.WORKLOADS["host1m_klt"]
+    n = 5000
+    P = 2
+    xs = [wl.keys_host(w, p, n=n) for p in range(P)]
+    qs = np.stack([wl.queries(w, p) for p in range(P)])
+    rots, lams = zip(*[orc.calib.klt_basis(wl.calibration_sample(w, p)) for p in range(P)])
+    rot = np.stack(rots)
+    lam = np.stack(lams)
+    say("end-to-end rotated small")
+    planes, scales = F.pack(bf16_dev(np.stack(xs)), rot=dev(rot))
+    pl, scores, out = _run_pipeline(F, planes, scales, n, dev(qs), dev(lam), w.budget, w.k, rot=dev(rot))
+    for p in range(P):
+        _compare_pair(orc, p, xs[p], qs[p], lam[p], w.budget, w.k, n, pl, scores, out,
+                      rot=rot[p], keys_rot=rot[p])
