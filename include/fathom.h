@@ -153,6 +153,51 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
                 int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
                 void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * fathom_scan_topk -- fathom_scan followed by fathom_topk in one call,
+ * without materialising the scores (the decode-step hot path).
+ *
+ * Same inputs as fathom_scan plus k, and the outputs of fathom_topk, which
+ * are identical to fathom_scan + fathom_topk on the same inputs.  Internally:
+ * the scores of every s-th block (s ~ sqrt(n / 4k), a power of two) are
+ * computed first and the exact k-th largest of that sample is taken as each
+ * head's threshold -- a lower bound of the true k-th largest, since the
+ * sample is a subset -- then one pass over the whole index keeps only the
+ * scores at or above it as candidates, and the k best candidates are
+ * selected exactly.  A head whose candidates exceed their capacity (possible
+ * only with massively tied scores) has its pair rescanned into a full score
+ * buffer inside the workspace and is selected from there; results are exact
+ * either way.
+ *   ws  device workspace of at least fathom_scan_topk_workspace_bytes(); it
+ *       includes that fallback buffer (P * G * npad floats), which is only
+ *       written when a capacity is exceeded.
+ * Errors: as fathom_scan and fathom_topk.
+ */
+size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k);
+int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
+                     const uint8_t* depth, const int16_t* active, const int32_t* n_active,
+                     const float* q_used, int32_t G, int32_t k, int32_t* topk_idx, float* topk_val,
+                     int32_t* union_idx, int32_t* union_len, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * fathom_scan_topk_stage -- the three stages of fathom_scan_topk as separate
+ * calls, so that a caller can time or interleave them.  Enqueueing stages 1,
+ * 2 and 3 in that order on one stream with the same arguments and workspace
+ * is exactly fathom_scan_topk.
+ *   stage 1: sample scores and per-head thresholds (written into ws)
+ *   stage 2: the scan over every block with the threshold filter -- one
+ *            kernel launch, the step's dominant kernel
+ *   stage 3: overflow repair, exact selection and union (the outputs; they
+ *            may be NULL in stages 1 and 2)
+ * Errors: ERR_ARG for a stage outside 1..3, else as fathom_scan_topk.
+ */
+int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t* scales, int32_t P,
+                           int32_t D, int64_t n, const uint8_t* depth, const int16_t* active,
+                           const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                           int32_t* topk_idx, float* topk_val, int32_t* union_idx,
+                           int32_t* union_len, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

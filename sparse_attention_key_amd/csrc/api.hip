@@ -115,4 +115,69 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
                                   (hipStream_t)stream));
 }
 
+size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k)
+{
+    if (P < 1 || G < 1 || G > kMaxG || n < 1 || k < 1 || k > n || k > kMaxK) return 0;
+    return topk_layout(P, G, n, k).bytes_fused;
+}
+
+static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
+                          int64_t n, const uint8_t* depth, const int16_t* active,
+                          const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                          int32_t* topk_idx, float* topk_val, int32_t* union_idx,
+                          int32_t* union_len, void* ws, size_t ws_bytes, void* stream, int stages)
+{
+    if (!planes || !scales || !depth || !active || !n_active || !q_used) return FATHOM_ERR_ARG;
+    if ((stages & 4) && (!topk_idx || !union_idx || !union_len)) return FATHOM_ERR_ARG;
+    int s = check_shape(P, n, D);
+    if (s) return s;
+    if (G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
+    if (k < 1 || k > n) return FATHOM_ERR_ARG;
+    if (k > kMaxK || G * k > kMaxUnion) return FATHOM_ERR_UNSUPPORTED;
+    const void* ps[] = {planes, scales, depth, active, n_active, q_used};
+    for (const void* p : ps)
+        if (!aligned16(p)) return FATHOM_ERR_ALIGN;
+    if (stages & 4) {
+        const void* os[] = {topk_idx, union_idx, union_len};
+        for (const void* p : os)
+            if (!aligned16(p)) return FATHOM_ERR_ALIGN;
+        if (topk_val && !aligned16(topk_val)) return FATHOM_ERR_ALIGN;
+    }
+    const TopkLayout L = topk_layout(P, G, n, k);
+    if (!ws || ws_bytes < L.bytes_fused) return FATHOM_ERR_WORKSPACE;
+    if (!aligned16(ws)) return FATHOM_ERR_ALIGN;
+    ScanArgs a{};
+    a.planes = planes;
+    a.scales = scales;
+    a.D = D;
+    a.n = n;
+    a.nb = (n + 63) / 64;
+    a.depth = depth;
+    a.active = active;
+    a.n_active = n_active;
+    a.q_used = q_used;
+    return hip_status(launch_scan_topk(a, P, G, k, topk_idx, topk_val, union_idx, union_len, ws, L,
+                                       stages, (hipStream_t)stream));
+}
+
+int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
+                     const uint8_t* depth, const int16_t* active, const int32_t* n_active,
+                     const float* q_used, int32_t G, int32_t k, int32_t* topk_idx, float* topk_val,
+                     int32_t* union_idx, int32_t* union_len, void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_topk_impl(planes, scales, P, D, n, depth, active, n_active, q_used, G, k, topk_idx,
+                          topk_val, union_idx, union_len, ws, ws_bytes, stream, 7);
+}
+
+int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t* scales, int32_t P,
+                           int32_t D, int64_t n, const uint8_t* depth, const int16_t* active,
+                           const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                           int32_t* topk_idx, float* topk_val, int32_t* union_idx,
+                           int32_t* union_len, void* ws, size_t ws_bytes, void* stream)
+{
+    if (stage < 1 || stage > 3) return FATHOM_ERR_ARG;
+    return scan_topk_impl(planes, scales, P, D, n, depth, active, n_active, q_used, G, k, topk_idx,
+                          topk_val, union_idx, union_len, ws, ws_bytes, stream, 1 << (stage - 1));
+}
+
 }  // extern "C"

@@ -108,15 +108,41 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, in
                        const uint8_t* depth, const int16_t* active, const int32_t* n_active,
                        const float* q_used, int G, float* scores, hipStream_t st);
 
+// Arguments of the scan kernels (see scan.hip).
+struct ScanArgs {
+    const uint64_t* planes;
+    const uint16_t* scales;
+    int D;
+    int64_t n, nb;
+    const uint8_t* depth;
+    const int16_t* active;
+    const int32_t* n_active;
+    const float* q_used;
+    int64_t stride;        // physical block = logical block * stride
+    int64_t nlb;           // logical blocks per pair
+    float* out;            // STORE: [P][G][nlb * 64]
+    const uint32_t* tau;   // FILTER: [P][G] key thresholds
+    uint32_t* counts;      // FILTER: [P][G]
+    uint64_t* cand;        // FILTER: [P][G][cap]
+    int64_t cap;
+    const uint32_t* only;  // optional [P] flags: pairs whose flag is 0 are skipped
+};
+hipError_t launch_scan_args(const ScanArgs& a, int P, int G, bool filter, hipStream_t st);
+
 struct TopkLayout {
-    int64_t m;       // selections = P * G
-    int64_t stride;  // sample every stride-th block
-    int64_t cap;     // candidate capacity per selection
-    size_t off_tau, off_count, off_cand, bytes;
+    int64_t m;           // selections = P * G
+    int64_t stride;      // sample every stride-th block
+    int64_t sample_nlb;  // sampled blocks per pair
+    int64_t cap;         // candidate capacity per selection
+    size_t off_tau, off_count, off_cand, bytes;        // top-k from given scores
+    size_t off_flags, off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };
 TopkLayout topk_layout(int P, int G, int64_t n, int k);
 hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,
                        float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
                        const TopkLayout& L, hipStream_t st);
+hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* topk_idx,
+                            float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
+                            const TopkLayout& L, int stages, hipStream_t st);
 
 }  // namespace fathom

@@ -2,94 +2,285 @@
 // write-up of Fathom: section "方法一" -- a t-plane prefix is the t-bit
 // mid-rise quantiser; section "方法二" -- only the first t_j planes of each
 // active channel are read, and the plan is shared by the G heads of a group
-// so the index is read once for all of them).
+// so the index is read once for all of them; limitations section -- one
+// shift-and-mask per extracted bit and G multiply-adds per element).
 //
 // Score contract: for token i and head h, s = 0 and for each active channel
 // j in ascending order s = fma(q_hj, khat_ij, s), with khat_ij the exact
 // dequantised prefix (2 c_t + 1 - 2^t) * 2^-t * scale.
 //
-// Simple form: one wavefront per 64-token block, lane i = token i, so every
-// plane word is wavefront-uniform; G float32 accumulators per lane.
+// Mapping (gfx950, wave64).  A lane owns TOK consecutive tokens of one
+// 64-token block (TOK = 32 for G <= 4, 16 for G <= 8, so that TOK * G = 128
+// fp32 accumulators per lane); the 64/TOK lanes of a block sit 64/TOK*... apart
+// so that one wavefront covers TOK consecutive blocks and every plane-word
+// load is one contiguous 256 B (TOK=32) or 128 B (TOK=16) row segment.  Codes
+// are extracted 4 (TOK=32) or 2 (TOK=16) tokens at a time: plane bit g of
+// every byte is shifted to its place in the code and masked in one
+// AND-OR, and v_cvt_f32_ubyte turns each byte into a float.  The next
+// channel's plane words and scale are in flight while the current channel is
+// accumulated.
+//
+// Two output modes: STORE writes the scores (all blocks, or every stride-th
+// block compacted -- the top-k threshold sample); FILTER compares each score
+// against the per-(pair, head) threshold and appends survivors as 64-bit
+// (key, ~index) composites with one atomic per wavefront and head.
 #include "common.h"
 
 namespace fathom {
 namespace {
 
-template <int G>
-__global__ __launch_bounds__(256) void scan_block_kernel(
-    const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int D, int64_t n,
-    int64_t nb, const uint8_t* __restrict__ depth, const int16_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, const float* __restrict__ q_used,
-    float* __restrict__ scores)
+constexpr int kScanThreads = 256;
+
+template <int TOK>
+struct Words;
+template <>
+struct Words<32> {
+    using T = uint32_t;
+};
+template <>
+struct Words<16> {
+    using T = uint16_t;
+};
+
+// Codes of the lane's TOK tokens for one channel, MSB-aligned: plane s sits
+// at bit 3 - s of its token's byte whatever the depth, so a t-plane prefix
+// reads as c4 = c_t * 2^(4-t) and absent planes stay zero.  Group g holds
+// tokens g, g+8, g+16, g+24 (one per byte; two bytes when TOK = 16).
+template <int TOK>
+__device__ __forceinline__ void codes(const uint32_t (&w)[4], int t, uint32_t (&c)[8])
 {
-    __shared__ float s_q[kMaxD][G];
-    __shared__ int s_j[kMaxD];
-    __shared__ int s_t[kMaxD];
-    const int p = blockIdx.y;
-    const int A = n_active[p];
-    for (int a = threadIdx.x; a < A; a += blockDim.x) {
-        const int j = active[(size_t)p * D + a];
-        s_j[a] = j;
-        s_t[a] = depth[(size_t)p * D + j];
+    constexpr uint32_t lanes = TOK == 32 ? 0x01010101u : 0x0101u;
 #pragma unroll
-        for (int h = 0; h < G; ++h) s_q[a][h] = q_used[((size_t)p * G + h) * D + j];
+    for (int g = 0; g < 8; ++g) c[g] = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if (s < t) {  // wavefront-uniform
+            const int pos = 3 - s;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const uint32_t x = (g >= pos) ? (w[s] >> (g - pos)) : (w[s] << (pos - g));
+                c[g] |= x & (lanes << pos);
+            }
+        }
+    }
+}
+
+// acc += q_h * khat for the lane's tokens, with khat = c4 * delta + c0 the
+// exact dequantised prefix (delta = scale/8, c0 = (1 - 2^t) * 2^-t * scale).
+template <int G, int TOK>
+__device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, float c0,
+                                           const float (&qv)[G], float (&acc)[TOK][G])
+{
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+#pragma unroll
+        for (int b = 0; b < TOK / 8; ++b) {
+            const float cf = (float)((c[g] >> (8 * b)) & 0xFFu);
+            const float kh = __builtin_fmaf(cf, delta, c0);  // exact
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[g + 8 * b][h] = __builtin_fmaf(qv[h], kh, acc[g + 8 * b][h]);
+        }
+    }
+}
+
+template <int G, int TOK, bool FILTER>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
+{
+    constexpr int kParts = 64 / TOK;       // lanes per block
+    constexpr int kBlocksPerWave = TOK;    // 64 / kParts
+    using WT = typename Words<TOK>::T;
+    __shared__ int s_jt[kMaxD];            // j | t << 16
+    __shared__ float s_q[kMaxD][G];
+    __shared__ __attribute__((aligned(16))) float s_stage[FILTER ? kScanThreads / kWave : 1][kWave][TOK + 4];
+
+    const int p = blockIdx.y;
+    if (a.only && a.only[p] == 0) return;
+    const int A = a.n_active[p];
+    for (int e = threadIdx.x; e < A; e += kScanThreads) {
+        const int j = a.active[(size_t)p * a.D + e];
+        s_jt[e] = j | ((int)a.depth[(size_t)p * a.D + j] << 16);
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_q[e][h] = a.q_used[((size_t)p * G + h) * a.D + j];
     }
     __syncthreads();
 
-    const int wave = threadIdx.x / kWave, lane = lane_id();
-    const int64_t b = (int64_t)blockIdx.x * 4 + wave;
-    if (b >= nb) return;
-    const uint64_t* pl = planes + (size_t)p * D * 4 * nb + b;
-    const uint16_t* sc = scales + (size_t)p * D * nb + b;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int part = lane / kBlocksPerWave;
+    const int64_t lb = ((int64_t)blockIdx.x * (kScanThreads / kWave) + wave) * kBlocksPerWave +
+                       (lane % kBlocksPerWave);
+    const int64_t lb0 = lb - (lane % kBlocksPerWave);
+    if (lb0 >= a.nlb) return;  // whole wavefront past the end
+    const bool live = lb < a.nlb;
+    const int64_t blk = (live ? lb : 0) * a.stride;
+    const int64_t nb = a.nb;
+    const WT* pw = reinterpret_cast<const WT*>(a.planes + (size_t)p * a.D * 4 * nb + blk) + part;
+    const uint16_t* ps = a.scales + (size_t)p * a.D * nb + blk;
+    constexpr int kWordStride = 8 / sizeof(WT);  // WT elements per 64-bit plane word
 
-    float acc[G];
+    float acc[TOK][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-    for (int a = 0; a < A; ++a) {
-        const int j = s_j[a], t = s_t[a];
-        const uint64_t* wj = pl + (size_t)j * 4 * nb;
-        uint32_t c = 0;
-        for (int s = 0; s < t; ++s) c = (c << 1) | (uint32_t)((wj[(size_t)s * nb] >> lane) & 1ull);
-        const float step = f16_bits_to_f32(sc[(size_t)j * nb]) * __uint_as_float((uint32_t)(127 - t) << 23);
-        const float kh = (float)((int)(2u * c + 1u) - (1 << t)) * step;
+    for (int i = 0; i < TOK; ++i)
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(s_q[a][h], kh, acc[h]);
+        for (int h = 0; h < G; ++h) acc[i][h] = 0.0f;
+
+    // software pipeline: words and scale of channel e+1 load during channel e
+    uint32_t wn0 = 0, wn1 = 0, wn2 = 0, wn3 = 0, scn = 0;
+    int jtn = 0;
+    if (A > 0) {
+        jtn = s_jt[0];
+        const int j = jtn & 0xFFFF, t = jtn >> 16;
+        const WT* src = pw + (size_t)j * 4 * nb * kWordStride;
+        const size_t ps_ = (size_t)nb * kWordStride;
+        wn0 = src[0];
+        wn1 = t > 1 ? (uint32_t)src[ps_] : 0u;
+        wn2 = t > 2 ? (uint32_t)src[2 * ps_] : 0u;
+        wn3 = t > 3 ? (uint32_t)src[3 * ps_] : 0u;
+        scn = ps[(size_t)j * nb];
     }
-    const int64_t tok = b * 64 + lane;
-    const int64_t npad = nb * 64;
+    for (int e = 0; e < A; ++e) {
+        const uint32_t w[4] = {wn0, wn1, wn2, wn3};
+        const uint32_t sc = scn;
+        const int t = jtn >> 16;
+        float qv[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-        scores[((size_t)p * G + h) * npad + tok] = tok < n ? acc[h] : -INFINITY;
+        for (int h = 0; h < G; ++h) qv[h] = s_q[e][h];
+        if (e + 1 < A) {
+            jtn = s_jt[e + 1];
+            const int j = jtn & 0xFFFF, tn = jtn >> 16;
+            const WT* src = pw + (size_t)j * 4 * nb * kWordStride;
+            const size_t ps_ = (size_t)nb * kWordStride;
+            wn0 = src[0];
+            wn1 = tn > 1 ? (uint32_t)src[ps_] : 0u;
+            wn2 = tn > 2 ? (uint32_t)src[2 * ps_] : 0u;
+            wn3 = tn > 3 ? (uint32_t)src[3 * ps_] : 0u;
+            scn = ps[(size_t)j * nb];
+        }
+        const float scf = f16_bits_to_f32(sc);
+        const float delta = scf * 0.125f;
+        const float c0 = scf * __uint_as_float((uint32_t)(127 - t) << 23) * (float)(1 - (1 << t));
+        uint32_t c[8];
+        codes<TOK>(w, t, c);
+        accumulate<G, TOK>(c, delta, c0, qv, acc);
+    }
+
+    const int64_t tok0 = blk * 64 + part * TOK;   // physical token of acc[0]
+    if (!FILTER) {
+        const int64_t row = a.nlb * 64;
+        const int64_t pos0 = lb * 64 + part * TOK;  // position in the output row
+        if (!live) return;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float* o = a.out + ((size_t)p * G + h) * row + pos0;
+#pragma unroll
+            for (int i = 0; i < TOK; i += 4) {
+                float4 v;
+                v.x = (tok0 + i + 0 < a.n) ? acc[i + 0][h] : -INFINITY;
+                v.y = (tok0 + i + 1 < a.n) ? acc[i + 1][h] : -INFINITY;
+                v.z = (tok0 + i + 2 < a.n) ? acc[i + 2][h] : -INFINITY;
+                v.w = (tok0 + i + 3 < a.n) ? acc[i + 3][h] : -INFINITY;
+                *reinterpret_cast<float4*>(o + i) = v;
+            }
+        }
+    } else {
+        // valid-token mask of the lane (only the last block is partial)
+        const int64_t nvalid = a.n - tok0;
+        const uint32_t vmask = !live || nvalid <= 0 ? 0u
+                               : (nvalid >= TOK ? (TOK == 32 ? 0xFFFFFFFFu : 0xFFFFu)
+                                                : ((1u << nvalid) - 1u));
+        float* stage = s_stage[wave][lane];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const size_t m = (size_t)p * G + h;
+            const uint32_t tk = a.tau[m];
+            // threshold as a float; +0 becomes -0 so that s - th keeps -0 scores
+            float th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
+            if (th == 0.0f) th = -0.0f;
+            // sign of fl(s - th) is 1 exactly when s < th: shift it into a mask
+            uint32_t fail = 0;
+#pragma unroll
+            for (int i = TOK - 1; i >= 0; --i)
+                fail = __builtin_amdgcn_alignbit(fail, __float_as_uint(acc[i][h] - th), 31);
+            uint32_t keep = ~fail & vmask;
+            const int cnt = __popc(keep);
+            int x = cnt;  // wavefront inclusive scan of cnt
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int y = __shfl_up(x, o, kWave);
+                if (lane >= o) x += y;
+            }
+            const int total = __shfl(x, kWave - 1, kWave);
+            if (total == 0) continue;
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&a.counts[m], (uint32_t)total);
+            base = __shfl(base, 0, kWave);
+            if (keep) {
+#pragma unroll
+                for (int i = 0; i < TOK; i += 4)
+                    *reinterpret_cast<float4*>(stage + i) =
+                        make_float4(acc[i][h], acc[i + 1][h], acc[i + 2][h], acc[i + 3][h]);
+            }
+            int64_t slot = (int64_t)base + (x - cnt);
+            uint64_t* dst = a.cand + m * a.cap;
+            while (keep) {
+                const int i = __ffs(keep) - 1;
+                keep &= keep - 1;
+                if (slot < a.cap) dst[slot] = composite(score_key(stage[i]), (uint32_t)(tok0 + i));
+                ++slot;
+            }
+        }
+    }
 }
 
-template <int G>
-hipError_t launch_g(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,
-                    const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                    const float* q_used, float* scores, hipStream_t st)
+template <int G, bool FILTER>
+hipError_t launch_g(const ScanArgs& a, int P, hipStream_t st)
 {
-    const int64_t nb = (n + 63) / 64;
-    dim3 grid((unsigned)((nb + 3) / 4), (unsigned)P);
-    scan_block_kernel<G><<<grid, 256, 0, st>>>(planes, scales, D, n, nb, depth, active, n_active,
-                                               q_used, scores);
+    constexpr int TOK = G <= 4 ? 32 : 16;
+    constexpr int per_wg = (kScanThreads / kWave) * TOK;  // blocks per workgroup
+    dim3 grid((unsigned)((a.nlb + per_wg - 1) / per_wg), (unsigned)P);
+    scan_kernel<G, TOK, FILTER><<<grid, kScanThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 
+template <bool FILTER>
+hipError_t launch_any(const ScanArgs& a, int P, int G, hipStream_t st)
+{
+    switch (G) {
+    case 1: return launch_g<1, FILTER>(a, P, st);
+    case 2: return launch_g<2, FILTER>(a, P, st);
+    case 3: return launch_g<3, FILTER>(a, P, st);
+    case 4: return launch_g<4, FILTER>(a, P, st);
+    case 5: return launch_g<5, FILTER>(a, P, st);
+    case 6: return launch_g<6, FILTER>(a, P, st);
+    case 7: return launch_g<7, FILTER>(a, P, st);
+    default: return launch_g<8, FILTER>(a, P, st);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_scan_args(const ScanArgs& a, int P, int G, bool filter, hipStream_t st)
+{
+    return filter ? launch_any<true>(a, P, G, st) : launch_any<false>(a, P, G, st);
+}
 
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,
                        const uint8_t* depth, const int16_t* active, const int32_t* n_active,
                        const float* q_used, int G, float* scores, hipStream_t st)
 {
-    switch (G) {
-    case 1: return launch_g<1>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    case 2: return launch_g<2>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    case 3: return launch_g<3>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    case 4: return launch_g<4>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    case 5: return launch_g<5>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    case 6: return launch_g<6>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    case 7: return launch_g<7>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    default: return launch_g<8>(planes, scales, P, D, n, depth, active, n_active, q_used, scores, st);
-    }
+    ScanArgs a{};
+    a.planes = planes;
+    a.scales = scales;
+    a.D = D;
+    a.n = n;
+    a.nb = (n + 63) / 64;
+    a.depth = depth;
+    a.active = active;
+    a.n_active = n_active;
+    a.q_used = q_used;
+    a.stride = 1;
+    a.nlb = a.nb;
+    a.out = scores;
+    return launch_any<false>(a, P, G, st);
 }
 
 }  // namespace fathom

@@ -176,6 +176,17 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt,
     if (i < cnt) p[i] = v;
 }
 
+// flags[p] = 1 when some head of pair p collected more candidates than fit.
+__global__ __launch_bounds__(256) void overflow_kernel(const uint32_t* __restrict__ counts, int P,
+                                                       int G, int64_t cap, uint32_t* __restrict__ flags)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= P) return;
+    uint32_t f = 0;
+    for (int h = 0; h < G; ++h) f |= (int64_t)counts[(size_t)p * G + h] > cap ? 1u : 0u;
+    flags[p] = f;
+}
+
 __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __restrict__ scores,
                                                                 int64_t n, int64_t npad,
                                                                 int64_t stride, int64_t count,
@@ -193,34 +204,39 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __r
     if (threadIdx.x == 0) tau[m] = (uint32_t)(T >> 32);
 }
 
+// Candidates of one (selection, 4096-token chunk).  blockIdx.x is the
+// selection, so neighbouring workgroups feed different counters; each
+// workgroup stages its survivors in LDS and takes its slots with a single
+// global atomic.
 __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ scores, int64_t n,
                                                      int64_t npad, const uint32_t* __restrict__ tau,
                                                      uint32_t* __restrict__ counts,
                                                      uint64_t* __restrict__ cand, int64_t cap)
 {
-    const int64_t m = blockIdx.y;
+    constexpr int kItems = 16;
+    __shared__ uint64_t s_c[256 * kItems];
+    __shared__ uint32_t s_n, s_base;
+    const int64_t m = blockIdx.x;
     const uint32_t th = tau[m];
     const float* s = scores + m * npad;
-    const int lane = lane_id();
-    const int64_t base = (int64_t)blockIdx.x * (256 * 16);
-    for (int r = 0; r < 16; ++r) {
+    const int64_t base = (int64_t)blockIdx.y * (256 * kItems);
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    for (int r = 0; r < kItems; ++r) {
         const int64_t tok = base + r * 256 + threadIdx.x;
-        bool pred = false;
-        uint32_t key = 0;
         if (tok < n) {
-            key = score_key(s[tok]);
-            pred = key >= th;
-        }
-        const uint64_t mask = __ballot(pred);
-        if (mask == 0) continue;
-        uint32_t slot0 = 0;
-        if (lane == __ffsll((long long)mask) - 1) slot0 = atomicAdd(&counts[m], (uint32_t)__popcll(mask));
-        slot0 = __shfl(slot0, __ffsll((long long)mask) - 1, kWave);
-        if (pred) {
-            const int64_t slot = (int64_t)slot0 + __popcll(mask & lanes_below(lane));
-            if (slot < cap) cand[m * cap + slot] = composite(key, (uint32_t)tok);
+            const uint32_t key = score_key(s[tok]);
+            if (key >= th) s_c[atomicAdd(&s_n, 1u)] = composite(key, (uint32_t)tok);
         }
     }
+    __syncthreads();
+    const uint32_t cnt = s_n;
+    if (cnt == 0) return;
+    if (threadIdx.x == 0) s_base = atomicAdd(&counts[m], cnt);
+    __syncthreads();
+    const int64_t b0 = s_base;
+    for (uint32_t i = threadIdx.x; i < cnt; i += 256)
+        if (b0 + i < cap) cand[m * cap + b0 + i] = s_c[i];
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
@@ -330,10 +346,16 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k)
     L.stride = s;
     L.cap = 8 * (int64_t)k * s + 1024;
     if (L.cap > nb * 64) L.cap = nb * 64;
+    L.sample_nlb = (nb + s - 1) / s;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     L.off_tau = 0;
-    L.off_count = (size_t)L.m * 4;
-    L.off_cand = ((L.off_count + (size_t)L.m * 4) + 255) & ~(size_t)255;
+    L.off_count = up((size_t)L.m * 4);
+    L.off_cand = up(L.off_count + (size_t)L.m * 4);
     L.bytes = L.off_cand + (size_t)L.m * (size_t)L.cap * 8;
+    L.off_flags = up(L.bytes);
+    L.off_sample = up(L.off_flags + (size_t)P * 4);
+    L.off_repair = up(L.off_sample + (size_t)L.m * (size_t)L.sample_nlb * 64 * 4);
+    L.bytes_fused = L.off_repair + (size_t)L.m * (size_t)nb * 64 * 4;
     return L;
 }
 
@@ -353,11 +375,67 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
     fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
     threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, L.stride,
                                                                  sblocks * 64, valid, k, tau);
-    filter_kernel<<<dim3((unsigned)((npad + 4095) / 4096), (unsigned)L.m), 256, 0, st>>>(
+    filter_kernel<<<dim3((unsigned)L.m, (unsigned)((npad + 4095) / 4096)), 256, 0, st>>>(
         scores, n, npad, tau, counts, cand, L.cap);
     select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
                                                               k, topk_idx, topk_val);
     union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(topk_idx, G, k, union_idx, union_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* topk_idx,
+                            float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
+                            const TopkLayout& L, int stages, hipStream_t st)
+{
+    const int64_t n = base.n, nb = base.nb, npad = nb * 64;
+    char* w = (char*)ws;
+    uint32_t* tau = (uint32_t*)(w + L.off_tau);
+    uint32_t* counts = (uint32_t*)(w + L.off_count);
+    uint64_t* cand = (uint64_t*)(w + L.off_cand);
+    uint32_t* flags = (uint32_t*)(w + L.off_flags);
+    float* sample = (float*)(w + L.off_sample);
+    float* repair = (float*)(w + L.off_repair);
+    const int64_t srow = L.sample_nlb * 64;
+    hipError_t e;
+    ScanArgs a = base;
+
+    if (stages & 1) {
+        // threshold: scores of every stride-th block, exact k-th largest
+        fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
+        a.stride = L.stride;
+        a.nlb = L.sample_nlb;
+        a.out = sample;
+        a.only = nullptr;
+        if ((e = launch_scan_args(a, P, G, false, st)) != hipSuccess) return e;
+        threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(sample, srow, srow, 1, srow,
+                                                                     srow, k, tau);
+    }
+    if (stages & 2) {
+        // filter: every block, keeping the scores at or above the threshold
+        a = base;
+        a.stride = 1;
+        a.nlb = nb;
+        a.tau = tau;
+        a.counts = counts;
+        a.cand = cand;
+        a.cap = L.cap;
+        a.only = nullptr;
+        if ((e = launch_scan_args(a, P, G, true, st)) != hipSuccess) return e;
+    }
+    if (stages & 4) {
+        // pairs whose candidates overflowed get their full scores recomputed
+        overflow_kernel<<<dim3((unsigned)((P + 255) / 256)), 256, 0, st>>>(counts, P, G, L.cap, flags);
+        a = base;
+        a.stride = 1;
+        a.nlb = nb;
+        a.out = repair;
+        a.only = flags;
+        if ((e = launch_scan_args(a, P, G, false, st)) != hipSuccess) return e;
+        // exact top-k of the candidates (or of the repaired scores), union
+        select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(repair, n, npad, counts, cand,
+                                                                  L.cap, k, topk_idx, topk_val);
+        union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(topk_idx, G, k, union_idx, union_len);
+    }
     return hipGetLastError();
 }
 

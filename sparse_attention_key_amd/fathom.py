@@ -50,7 +50,12 @@ def lib() -> ctypes.CDLL:
         L.fathom_topk_workspace_bytes.argtypes = [i32, i32, i64, i32]
         L.fathom_topk_workspace_bytes.restype = sz
         L.fathom_topk.argtypes = [P, i32, i32, i64, i32, P, P, P, P, P, sz, P]
-        for f in (L.fathom_pack, L.fathom_plan, L.fathom_scan, L.fathom_topk):
+        L.fathom_scan_topk_workspace_bytes.argtypes = [i32, i32, i64, i32]
+        L.fathom_scan_topk_workspace_bytes.restype = sz
+        L.fathom_scan_topk.argtypes = [P, P, i32, i32, i64, P, P, P, P, i32, i32, P, P, P, P, P, sz, P]
+        L.fathom_scan_topk_stage.argtypes = [i32] + L.fathom_scan_topk.argtypes
+        for f in (L.fathom_pack, L.fathom_plan, L.fathom_scan, L.fathom_topk, L.fathom_scan_topk,
+                  L.fathom_scan_topk_stage):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,14 +153,20 @@ def topk_workspace_bytes(P: int, G: int, n: int, k: int) -> int:
     return int(lib().fathom_topk_workspace_bytes(P, G, int(n), int(k)))
 
 
+def scan_topk_workspace_bytes(P: int, G: int, n: int, k: int) -> int:
+    return int(lib().fathom_scan_topk_workspace_bytes(P, G, int(n), int(k)))
+
+
 class TopkOut:
-    def __init__(self, P: int, G: int, n: int, k: int, device="cuda", with_values=True):
+    def __init__(self, P: int, G: int, n: int, k: int, device="cuda", with_values=True,
+                 fused: bool = False):
         self.P, self.G, self.n, self.k = P, G, n, k
         self.idx = torch.empty((P, G, k), dtype=torch.int32, device=device)
         self.val = torch.empty((P, G, k), dtype=torch.float32, device=device) if with_values else None
         self.union = torch.empty((P, G * k), dtype=torch.int32, device=device)
         self.union_len = torch.empty((P,), dtype=torch.int32, device=device)
-        nbytes = max(topk_workspace_bytes(P, G, n, k), 16)
+        ws_fn = scan_topk_workspace_bytes if fused else topk_workspace_bytes
+        nbytes = max(ws_fn(P, G, n, k), 16)
         self.ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
 
@@ -170,3 +181,29 @@ def topk_into(scores, n: int, out: TopkOut, stream=None):
 def topk(scores, n: int, k: int, stream=None) -> TopkOut:
     P, G, _ = scores.shape
     return topk_into(scores, n, TopkOut(P, G, n, k, scores.device), stream)
+
+
+# ------------------------------------------------------- fused scan + top-k
+
+def scan_topk_into(planes, scales, n: int, pl: Plan, out: TopkOut, stream=None):
+    """Scores, top-k and union of every pair without materialising scores;
+    `out` must be a TopkOut(..., fused=True)."""
+    _check("fathom_scan_topk", lib().fathom_scan_topk(
+        _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _ptr(pl.depth), _ptr(pl.active),
+        _ptr(pl.n_active), _ptr(pl.q_used), pl.G, out.k, _ptr(out.idx), _ptr(out.val), _ptr(out.union),
+        _ptr(out.union_len), _ptr(out.ws), out.ws.numel(), _stream(stream)))
+    return out
+
+
+def scan_topk(planes, scales, n: int, pl: Plan, k: int, stream=None) -> TopkOut:
+    out = TopkOut(pl.P, pl.G, n, k, pl.q_used.device, fused=True)
+    return scan_topk_into(planes, scales, n, pl, out, stream)
+
+
+def scan_topk_stage(stage: int, planes, scales, n: int, pl: Plan, out: TopkOut, stream=None):
+    """One stage (1 threshold, 2 filtered scan, 3 select + union) of scan_topk_into."""
+    _check("fathom_scan_topk_stage", lib().fathom_scan_topk_stage(
+        int(stage), _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _ptr(pl.depth), _ptr(pl.active),
+        _ptr(pl.n_active), _ptr(pl.q_used), pl.G, out.k, _ptr(out.idx), _ptr(out.val), _ptr(out.union),
+        _ptr(out.union_len), _ptr(out.ws), out.ws.numel(), _stream(stream)))
+    return out

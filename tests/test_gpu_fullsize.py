@@ -1,0 +1,145 @@
+"""Full-size GPU runs in the benchmark's launch configuration (all 288 layer x
+KV-head pairs in one call): every pair is checked through properties that
+hold at any size, and sampled pairs are recomputed by the oracle from the same
+generator keys and compared bit for bit.
+
+Workloads: the 131k-token sweep (B in 32..136 plus the 136-bit fixed plan)
+and the 1M-token step.
+"""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_util import need_gpu, say, u16, u64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    need_gpu()
+    from sparse_attention_key_amd import fathom
+
+    fathom.lib()
+    return fathom
+
+
+def _index(F, w):
+    planes = torch.empty((w.P, w.D, 4, w.nb), dtype=torch.int64, device="cuda")
+    scales = torch.empty((w.P, w.D, w.nb), dtype=torch.int16, device="cuda")
+    for p0 in range(0, w.P, 16):
+        pairs = list(range(p0, min(w.P, p0 + 16)))
+        keys = wl.keys_device(w, pairs)
+        F.pack_into(keys, planes[p0:p0 + len(pairs)], scales[p0:p0 + len(pairs)])
+        del keys
+    torch.cuda.synchronize()
+    return planes, scales
+
+
+def _inputs(orc, w):
+    q = np.stack([wl.queries(w, p) for p in range(w.P)])
+    s2 = np.stack([orc.calib.channel_variance(wl.calibration_sample(w, p)) for p in range(w.P)])
+    return q, s2
+
+
+def _check_properties(w, budget, mode, pl, scores, out):
+    """Plan, top-k and union validity for every pair, on the GPU."""
+    P, G, n, k = w.P, w.G, w.n, w.k
+    depth = pl.depth.to(torch.int64)
+    assert int(depth.max()) <= 4
+    if mode == 0:
+        assert bool((depth.sum(1) <= budget).all())
+    else:
+        assert bool((depth.sum(1) == 4 * budget).all())
+    assert bool((pl.n_active == (depth > 0).sum(1)).all())
+    idx = out.idx.to(torch.int64)
+    assert int(idx.min()) >= 0 and int(idx.max()) < n
+    s = scores[..., :n]
+    got = torch.gather(s, 2, idx)
+    assert torch.equal(got, out.val) or bool(((got == out.val) | ((got == 0) & (out.val == 0))).all())
+    assert bool((out.val[..., 1:] <= out.val[..., :-1]).all())  # ordered
+    kth = out.val[..., -1:]
+    above = (s > kth).sum(-1)
+    at_least = (s >= kth).sum(-1)
+    assert bool((above < k).all()) and bool((at_least >= k).all())  # exactly the top-k values
+    srt = torch.sort(idx, dim=-1).values
+    assert bool((srt[..., 1:] != srt[..., :-1]).all())  # unique per head
+    ul = out.union_len.to(torch.int64)
+    assert bool((ul <= G * k).all())
+    for p in range(0, P, max(1, P // 16)):
+        u = torch.unique(idx[p])
+        assert int(ul[p]) == u.numel() and torch.equal(out.union[p, : u.numel()].to(torch.int64), u)
+
+
+def _oracle_pair(orc, w, p, q, s2, budget, mode):
+    x = wl.keys_device(w, [p])[0].float().cpu().numpy()  # generator output
+    rp, rs = orc.pack(x)
+    del x
+    ref = orc.step(rp, rs, w.n, q[p], s2[p], budget, w.k, mode=mode)
+    return p, rp, rs, ref
+
+
+def _compare_sampled(orc, w, sample, q, s2, budget, mode, planes, scales, pl, scores, out):
+    with cf.ThreadPoolExecutor(max_workers=len(sample)) as ex:
+        refs = list(ex.map(lambda p: _oracle_pair(orc, w, p, q, s2, budget, mode), sample))
+    for p, rp, rs, ref in refs:
+        say("compare pair", p)
+        assert np.array_equal(u64(planes[p]), rp)
+        assert np.array_equal(u16(scales[p]), rs)
+        assert np.array_equal(pl.depth[p].cpu().numpy(), ref["depth"])
+        assert np.array_equal(scores[p].cpu().numpy().view(np.uint32), ref["scores"].view(np.uint32))
+        assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"])
+        assert int(out.union_len[p]) == ref["union_len"]
+        assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+
+
+@pytest.fixture(scope="module")
+def sweep131k(F, orc):
+    w = wl.WORKLOADS["sweep131k"]
+    say("building 131k index, 288 pairs")
+    planes, scales = _index(F, w)
+    q, s2 = _inputs(orc, w)
+    yield w, planes, scales, q, s2
+    del planes, scales
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode,budget", [(0, 32), (0, 48), (0, 68), (0, 92), (0, 136), (1, 32)])
+def test_sweep131k(F, orc, sweep131k, mode, budget):
+    w, planes, scales, q, s2 = sweep131k
+    say("131k sweep", mode, budget)
+    pl = F.plan(torch.from_numpy(q).cuda(), torch.from_numpy(s2).cuda(), budget, mode)
+    scores = F.scan(planes, scales, w.n, pl)
+    out = F.topk(scores, w.n, w.k)
+    torch.cuda.synchronize()
+    _check_properties(w, budget, mode, pl, scores, out)
+    fused = F.scan_topk(planes, scales, w.n, pl, w.k)
+    assert torch.equal(fused.idx, out.idx) and torch.equal(fused.union, out.union)
+    assert torch.equal(fused.union_len, out.union_len)
+    del fused
+    sample = [7, 200] if budget != 48 else [0, 101, 287]
+    _compare_sampled(orc, w, sample, q, s2, budget, mode, planes, scales, pl, scores, out)
+    del scores, out
+    torch.cuda.empty_cache()
+
+
+def test_long1m_step(F, orc):
+    w = wl.WORKLOADS["long1m"]
+    say("building 1M index, 288 pairs (20.5 GB)")
+    planes, scales = _index(F, w)
+    q, s2 = _inputs(orc, w)
+    say("1M step")
+    pl = F.plan(torch.from_numpy(q).cuda(), torch.from_numpy(s2).cuda(), w.budget, 0)
+    scores = F.scan(planes, scales, w.n, pl)
+    out = F.topk(scores, w.n, w.k)
+    torch.cuda.synchronize()
+    _check_properties(w, w.budget, 0, pl, scores, out)
+    fused = F.scan_topk(planes, scales, w.n, pl, w.k)
+    assert torch.equal(fused.idx, out.idx) and torch.equal(fused.union, out.union)
+    del fused
+    _compare_sampled(orc, w, [3, 150, 286], q, s2, w.budget, 0, planes, scales, pl, scores, out)
+    del planes, scales, scores, out
+    torch.cuda.empty_cache()

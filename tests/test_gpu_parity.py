@@ -265,3 +265,38 @@ def test_end_to_end_rotated_small(F, orc):
     for p in range(P):
         _compare_pair(orc, p, xs[p], qs[p], lam[p], w.budget, w.k, n, pl, scores, out,
                       rot=rot[p], keys_rot=rot[p])
+
+
+FUSED_CASES = [  # (workload-ish, n, D, G, budget, k, mode)
+    ("rand", 4096, 128, 4, 48, 64, 0), ("rand", 32768 + 17, 128, 4, 48, 512, 0),
+    ("rand", 700, 128, 4, 48, 512, 0), ("rand", 5000, 64, 8, 92, 256, 0),
+    ("rand", 20000, 128, 4, 0, 300, 0),      # every score 0: ties overflow -> repair path
+    ("rand", 9000, 128, 2, 32, 1, 1), ("rand", 100, 128, 4, 2, 100, 2), ("rand", 1, 128, 4, 48, 1, 0),
+]
+
+
+@pytest.mark.parametrize("kind,n,D,G,budget,k,mode", FUSED_CASES)
+def test_fused_scan_topk_bit_exact(F, orc, kind, n, D, G, budget, k, mode):
+    P = 3
+    g = np.random.default_rng(n * 7 + budget + k)
+    x = [(g.standard_normal((n, D)) * np.exp(0.7 * g.standard_normal(D))).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, n + 1)
+    say("fused scan+top-k", n, D, G, budget, k, mode)
+    planes, scales = F.pack(dev(np.stack(x)))
+    pl = F.plan(dev(q), dev(s2), budget, mode)
+    out = F.scan_topk(planes, scales, n, pl, k)
+    staged = F.TopkOut(P, G, n, k, "cuda", fused=True)
+    for stage in (1, 2, 3):
+        F.scan_topk_stage(stage, planes, scales, n, pl, staged)
+    idx = out.idx.cpu().numpy()
+    val = out.val.cpu().numpy()
+    assert np.array_equal(idx, staged.idx.cpu().numpy())
+    assert np.array_equal(out.union.cpu().numpy(), staged.union.cpu().numpy())
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        ref = orc.step(rp, rs, n, q[p], s2[p], budget, k, mode=mode)
+        assert np.array_equal(idx[p], ref["topk"]), p
+        for h in range(G):
+            assert np.array_equal(val[p, h], ref["scores"][h][ref["topk"][h]])
+        assert int(out.union_len[p]) == ref["union_len"]
+        assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
