@@ -118,22 +118,24 @@ struct ScanArgs {
     const int16_t* active;
     const int32_t* n_active;
     const float* q_used;
-    int64_t stride;        // physical block = logical block * stride
-    int64_t nlb;           // logical blocks per pair
-    float* out;            // STORE: [P][G][nlb * 64]
+    int64_t stride;        // 1, or: scan one run of 32 consecutive blocks in every stride runs
+    int64_t nlb;           // logical blocks per pair (rows of the STORE output / 64)
+    float* out;            // STORE: [P][G][nlb * 64]; LANEMAX: [P][G][nlb * (64 / TOK)]
     const uint32_t* tau;   // FILTER: [P][G] key thresholds
     uint32_t* counts;      // FILTER: [P][G]
     uint64_t* cand;        // FILTER: [P][G][cap]
     int64_t cap;
     const uint32_t* only;  // optional [P] flags: pairs whose flag is 0 are skipped
 };
-hipError_t launch_scan_args(const ScanArgs& a, int P, int G, bool filter, hipStream_t st);
+// mode: 0 store scores, 1 filter into candidates, 2 per-lane maxima
+hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream_t st);
 
 struct TopkLayout {
     int64_t m;           // selections = P * G
-    int64_t stride;      // sample every stride-th block
-    int64_t sample_nlb;  // sampled blocks per pair
+    int64_t stride;      // sample one run of 32 blocks in every `stride` runs
+    int64_t sample_nlb;  // logical sample blocks per pair (whole runs)
     int64_t cap;         // candidate capacity per selection
+    bool lanemax;        // fused threshold from per-lane maxima of the sample
     size_t off_tau, off_count, off_cand, bytes;        // top-k from given scores
     size_t off_flags, off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };

@@ -20,16 +20,18 @@
 // channel's plane words and scale are in flight while the current channel is
 // accumulated.
 //
-// Two output modes: STORE writes the scores (all blocks, or every stride-th
-// block compacted -- the top-k threshold sample); FILTER compares each score
-// against the per-(pair, head) threshold and appends survivors as 64-bit
-// (key, ~index) composites with one atomic per wavefront and head.
+// Output modes: STORE writes the scores; FILTER compares each score against
+// the per-(pair, head) threshold and appends survivors as 64-bit
+// (key, ~index) composites with one atomic per wavefront and head; LANEMAX
+// writes, per lane and head, the largest score among the lane's tokens (over
+// a sample of blocks: the input of the top-k threshold).
 #include "common.h"
 
 namespace fathom {
 namespace {
 
 constexpr int kScanThreads = 256;
+constexpr int kRun = 32;  // sampled blocks come in runs of this many consecutive blocks
 
 template <int TOK>
 struct Words;
@@ -83,7 +85,9 @@ __device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, 
     }
 }
 
-template <int G, int TOK, bool FILTER>
+enum { kStore = 0, kFilter = 1, kLaneMax = 2 };
+
+template <int G, int TOK, int MODE>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
 {
     constexpr int kParts = 64 / TOK;       // lanes per block
@@ -91,6 +95,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     using WT = typename Words<TOK>::T;
     __shared__ int s_jt[kMaxD];            // j | t << 16
     __shared__ float s_q[kMaxD][G];
+    constexpr bool FILTER = MODE == kFilter;
     __shared__ __attribute__((aligned(16))) float s_stage[FILTER ? kScanThreads / kWave : 1][kWave][TOK + 4];
 
     const int p = blockIdx.y;
@@ -110,8 +115,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
                        (lane % kBlocksPerWave);
     const int64_t lb0 = lb - (lane % kBlocksPerWave);
     if (lb0 >= a.nlb) return;  // whole wavefront past the end
-    const bool live = lb < a.nlb;
-    const int64_t blk = (live ? lb : 0) * a.stride;
+    // logical -> physical block: runs of kRun consecutive blocks, one run in
+    // every `stride` (stride 1 is the identity)
+    const int64_t phys = (lb / kRun) * kRun * a.stride + (lb % kRun);
+    const bool live = lb < a.nlb && phys < a.nb;
+    const int64_t blk = live ? phys : 0;
     const int64_t nb = a.nb;
     const WT* pw = reinterpret_cast<const WT*>(a.planes + (size_t)p * a.D * 4 * nb + blk) + part;
     const uint16_t* ps = a.scales + (size_t)p * a.D * nb + blk;
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
             wn3 = tn > 3 ? (uint32_t)src[3 * ps_] : 0u;
             scn = ps[(size_t)j * nb];
         }
-        const float scf = f16_bits_to_f32(sc);
+        const float scf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc);  // v_cvt_f32_f16, exact
         const float delta = scf * 0.125f;
         const float c0 = scf * __uint_as_float((uint32_t)(127 - t) << 23) * (float)(1 - (1 << t));
         uint32_t c[8];
@@ -164,20 +172,32 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     }
 
     const int64_t tok0 = blk * 64 + part * TOK;   // physical token of acc[0]
-    if (!FILTER) {
+    if (MODE == kLaneMax) {
+        // one value per lane and head: the max score of the lane's valid tokens
+        if (lb >= a.nlb) return;
+        const int64_t row = a.nlb * kParts;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < TOK; ++i)
+                mx = (live && tok0 + i < a.n) ? fmaxf(mx, acc[i][h]) : mx;
+            a.out[((size_t)p * G + h) * row + lb * kParts + part] = mx;
+        }
+    } else if (!FILTER) {
         const int64_t row = a.nlb * 64;
         const int64_t pos0 = lb * 64 + part * TOK;  // position in the output row
-        if (!live) return;
+        if (lb >= a.nlb) return;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float* o = a.out + ((size_t)p * G + h) * row + pos0;
 #pragma unroll
             for (int i = 0; i < TOK; i += 4) {
                 float4 v;
-                v.x = (tok0 + i + 0 < a.n) ? acc[i + 0][h] : -INFINITY;
-                v.y = (tok0 + i + 1 < a.n) ? acc[i + 1][h] : -INFINITY;
-                v.z = (tok0 + i + 2 < a.n) ? acc[i + 2][h] : -INFINITY;
-                v.w = (tok0 + i + 3 < a.n) ? acc[i + 3][h] : -INFINITY;
+                v.x = (live && tok0 + i + 0 < a.n) ? acc[i + 0][h] : -INFINITY;
+                v.y = (live && tok0 + i + 1 < a.n) ? acc[i + 1][h] : -INFINITY;
+                v.z = (live && tok0 + i + 2 < a.n) ? acc[i + 2][h] : -INFINITY;
+                v.w = (live && tok0 + i + 3 < a.n) ? acc[i + 3][h] : -INFINITY;
                 *reinterpret_cast<float4*>(o + i) = v;
             }
         }
@@ -231,36 +251,38 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     }
 }
 
-template <int G, bool FILTER>
+template <int G, int MODE>
 hipError_t launch_g(const ScanArgs& a, int P, hipStream_t st)
 {
     constexpr int TOK = G <= 4 ? 32 : 16;
     constexpr int per_wg = (kScanThreads / kWave) * TOK;  // blocks per workgroup
     dim3 grid((unsigned)((a.nlb + per_wg - 1) / per_wg), (unsigned)P);
-    scan_kernel<G, TOK, FILTER><<<grid, kScanThreads, 0, st>>>(a);
+    scan_kernel<G, TOK, MODE><<<grid, kScanThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 
-template <bool FILTER>
+template <int MODE>
 hipError_t launch_any(const ScanArgs& a, int P, int G, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_g<1, FILTER>(a, P, st);
-    case 2: return launch_g<2, FILTER>(a, P, st);
-    case 3: return launch_g<3, FILTER>(a, P, st);
-    case 4: return launch_g<4, FILTER>(a, P, st);
-    case 5: return launch_g<5, FILTER>(a, P, st);
-    case 6: return launch_g<6, FILTER>(a, P, st);
-    case 7: return launch_g<7, FILTER>(a, P, st);
-    default: return launch_g<8, FILTER>(a, P, st);
+    case 1: return launch_g<1, MODE>(a, P, st);
+    case 2: return launch_g<2, MODE>(a, P, st);
+    case 3: return launch_g<3, MODE>(a, P, st);
+    case 4: return launch_g<4, MODE>(a, P, st);
+    case 5: return launch_g<5, MODE>(a, P, st);
+    case 6: return launch_g<6, MODE>(a, P, st);
+    case 7: return launch_g<7, MODE>(a, P, st);
+    default: return launch_g<8, MODE>(a, P, st);
     }
 }
 
 }  // namespace
 
-hipError_t launch_scan_args(const ScanArgs& a, int P, int G, bool filter, hipStream_t st)
+hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream_t st)
 {
-    return filter ? launch_any<true>(a, P, G, st) : launch_any<false>(a, P, G, st);
+    if (mode == kFilter) return launch_any<kFilter>(a, P, G, st);
+    if (mode == kLaneMax) return launch_any<kLaneMax>(a, P, G, st);
+    return launch_any<kStore>(a, P, G, st);
 }
 
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,
@@ -280,7 +302,7 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, in
     a.stride = 1;
     a.nlb = a.nb;
     a.out = scores;
-    return launch_any<false>(a, P, G, st);
+    return launch_any<kStore>(a, P, G, st);
 }
 
 }  // namespace fathom

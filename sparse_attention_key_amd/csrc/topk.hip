@@ -8,9 +8,11 @@
 // exact answer with ties already broken.
 //
 // Pipeline per call (one selection = one (pair, head)):
-//  1. threshold: exact k-th largest composite of a SAMPLE of the tokens (every
-//     stride-th block).  Its key is a lower bound of the true k-th largest
-//     key, because the sample is a subset: every true winner passes it.
+//  1. threshold: exact k-th largest of a SAMPLE of scores (one run of 32
+//     consecutive blocks in every `stride` runs; in the fused path, the
+//     maximum of each lane's 32 or 16 tokens of those blocks).  Each sample
+//     value is a distinct token's score, so the k-th largest sample value is
+//     a lower bound of the true k-th largest: every true winner passes it.
 //  2. filter:    one pass over all scores appends key >= threshold to a
 //                candidate list (wavefront-aggregated atomics).
 //  3. select:    exact k largest composites of the candidates (radix select
@@ -33,16 +35,18 @@ struct SelShared {
     uint32_t wsum[kSelThreads / kWave];
     uint32_t nbuf;
     uint32_t bin, above, inbin;
+    uint64_t result;
 };
 
 struct DenseSrc {
     const float* s;
     int64_t n;       // valid tokens
-    int64_t stride;  // sample every stride-th block (1 = all)
+    int64_t stride;  // one run of 32 blocks in every `stride` runs (1 = all)
     int64_t count;   // elements enumerated
     __device__ __forceinline__ uint64_t get(int64_t e, bool& ok) const
     {
-        const int64_t tok = (e >> 6) * stride * 64 + (e & 63);
+        const int64_t lb = e >> 6;
+        const int64_t tok = ((lb >> 5) * stride * 32 + (lb & 31)) * 64 + (e & 63);
         ok = tok < n;
         const float v = ok ? s[tok] : 0.0f;
         return composite(score_key(v), (uint32_t)tok);
@@ -77,27 +81,6 @@ __device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh)
     return off + x - v;
 }
 
-// Bitonic sort of buf[0..len) descending (len a power of two, <= kBuf).
-__device__ void bitonic_desc(uint64_t* buf, int len)
-{
-    for (int k2 = 2; k2 <= len; k2 <<= 1) {
-        for (int j = k2 >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < len; i += blockDim.x) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint64_t a = buf[i], b = buf[ixj];
-                    const bool desc = (i & k2) == 0;
-                    if (desc ? (a < b) : (a > b)) {
-                        buf[i] = b;
-                        buf[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 __device__ __forceinline__ int pow2_ceil(int x)
 {
     int p = 1;
@@ -105,69 +88,96 @@ __device__ __forceinline__ int pow2_ceil(int x)
     return p;
 }
 
-// Exact need-th largest (1-based) of the unique composites of src.
+// One radix level: histogram of the 11-bit digit at `sft` over the elements
+// matching (prefix, pmask); picks the bin holding the need-th largest and
+// narrows prefix/pmask/need.  Returns the number of elements in that bin.
+template <class Src>
+__device__ uint32_t radix_level(const Src& src, int sft, uint32_t wm, uint64_t& prefix,
+                                uint64_t& pmask, int& need, SelShared& sh)
+{
+    for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[i] = 0;
+    if (threadIdx.x == 0) {
+        sh.bin = 0;
+        sh.above = 0;
+        sh.inbin = 0;
+    }
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
+        bool ok;
+        const uint64_t v = src.get(e, ok);
+        if (ok && (v & pmask) == prefix) atomicAdd(&sh.hist[(uint32_t)(v >> sft) & wm], 1u);
+    }
+    __syncthreads();
+    // reversed bins 2t, 2t+1 -> bins 2047-2t, 2046-2t (top first)
+    const int t = threadIdx.x;
+    const uint32_t c0 = sh.hist[kBins - 1 - 2 * t], c1 = sh.hist[kBins - 2 - 2 * t];
+    const uint32_t ex = block_excl_scan(c0 + c1, sh);
+    if (ex < (uint32_t)need && (uint32_t)need <= ex + c0) {
+        sh.bin = kBins - 1 - 2 * t;
+        sh.above = ex;
+        sh.inbin = c0;
+    } else if (ex + c0 < (uint32_t)need && (uint32_t)need <= ex + c0 + c1) {
+        sh.bin = kBins - 2 - 2 * t;
+        sh.above = ex + c0;
+        sh.inbin = c1;
+    }
+    __syncthreads();
+    const uint32_t bin = sh.bin, inbin = sh.inbin;
+    need -= (int)sh.above;
+    prefix |= (uint64_t)bin << sft;
+    pmask |= (uint64_t)wm << sft;
+    __syncthreads();
+    return inbin;
+}
+
+struct LdsSrc {
+    const uint64_t* c;
+    int64_t count;
+    __device__ __forceinline__ uint64_t get(int64_t e, bool& ok) const
+    {
+        ok = true;
+        return c[e];
+    }
+};
+
+// Exact need-th largest (1-based) of the unique composites of src: 11-bit
+// radix levels over src until the bin that holds it fits in LDS, then the
+// remaining levels over that LDS copy.
 template <class Src>
 __device__ uint64_t kth_largest(const Src& src, int need, SelShared& sh)
 {
     uint64_t prefix = 0, pmask = 0;
     const int shifts[6] = {53, 42, 31, 20, 9, 0};
-    for (int lvl = 0; lvl < 6; ++lvl) {
-        const int sft = shifts[lvl];
-        const uint32_t wm = (lvl == 5) ? 0x1FFu : 0x7FFu;
-        for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[i] = 0;
-        __syncthreads();
-        for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
-            bool ok;
-            const uint64_t v = src.get(e, ok);
-            if (ok && (v & pmask) == prefix) atomicAdd(&sh.hist[(uint32_t)(v >> sft) & wm], 1u);
-        }
-        __syncthreads();
-        // reversed bins 2t, 2t+1 -> bins 2047-2t, 2046-2t (top first)
-        const int t = threadIdx.x;
-        if (t == 0) {
-            sh.bin = 0;
-            sh.above = 0;
-            sh.inbin = 0;
-        }
-        const uint32_t c0 = sh.hist[kBins - 1 - 2 * t], c1 = sh.hist[kBins - 2 - 2 * t];
-        const uint32_t ex = block_excl_scan(c0 + c1, sh);
-        if (ex < (uint32_t)need && (uint32_t)need <= ex + c0) {
-            sh.bin = kBins - 1 - 2 * t;
-            sh.above = ex;
-            sh.inbin = c0;
-        } else if (ex + c0 < (uint32_t)need && (uint32_t)need <= ex + c0 + c1) {
-            sh.bin = kBins - 2 - 2 * t;
-            sh.above = ex + c0;
-            sh.inbin = c1;
-        }
-        __syncthreads();
-        const uint32_t bin = sh.bin, inbin = sh.inbin;
-        need -= (int)sh.above;
-        prefix |= (uint64_t)bin << sft;
-        pmask |= (uint64_t)wm << sft;
-        __syncthreads();
-        if (inbin <= (uint32_t)kBuf) {
-            if (threadIdx.x == 0) sh.nbuf = 0;
-            __syncthreads();
-            for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
-                bool ok;
-                const uint64_t v = src.get(e, ok);
-                if (ok && (v & pmask) == prefix) {
-                    const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
-                    if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
-                }
-            }
-            __syncthreads();
-            const int len = pow2_ceil((int)inbin);
-            for (int i = (int)inbin + threadIdx.x; i < len; i += blockDim.x) sh.buf[i] = 0;
-            __syncthreads();
-            bitonic_desc(sh.buf, len);
-            const uint64_t T = sh.buf[need < 1 ? 0 : (need > kBuf ? kBuf - 1 : need - 1)];
-            __syncthreads();
-            return T;
+    int lvl = 0;
+    uint32_t inbin = 0;
+    for (; lvl < 6; ++lvl) {
+        inbin = radix_level(src, shifts[lvl], lvl == 5 ? 0x1FFu : 0x7FFu, prefix, pmask, need, sh);
+        if (inbin <= (uint32_t)kBuf) break;
+    }
+    // gather the bin into LDS
+    if (threadIdx.x == 0) sh.nbuf = 0;
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
+        bool ok;
+        const uint64_t v = src.get(e, ok);
+        if (ok && (v & pmask) == prefix) {
+            const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
+            if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
         }
     }
-    return prefix;  // not reached: the last digit isolates a single composite
+    __syncthreads();
+    const LdsSrc lsrc{sh.buf, (int64_t)(inbin < (uint32_t)kBuf ? inbin : kBuf)};
+    for (++lvl; lvl < 6 && inbin > 1; ++lvl)
+        inbin = radix_level(lsrc, shifts[lvl], lvl == 5 ? 0x1FFu : 0x7FFu, prefix, pmask, need, sh);
+    // the single element with this prefix
+    if (threadIdx.x == 0) sh.result = 0;
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < lsrc.count; e += blockDim.x)
+        if ((sh.buf[e] & pmask) == prefix) sh.result = sh.buf[e];
+    __syncthreads();
+    const uint64_t T = sh.result;
+    __syncthreads();
+    return T;
 }
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt, uint32_t v)
@@ -252,7 +262,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     DenseSrc dsrc{scores + m * npad, n, 1, npad};
     CandSrc csrc{cand + m * cap, cnt};
     T = dense ? kth_largest(dsrc, k, sh) : kth_largest(csrc, k, sh);
-    // gather the k winners (composites >= T) and sort them
+    // gather the k winners (composites >= T); each one's rank among them is
+    // its output position (composites are unique)
     if (threadIdx.x == 0) sh.nbuf = 0;
     __syncthreads();
     const int64_t total = dense ? dsrc.count : csrc.count;
@@ -265,14 +276,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
     __syncthreads();
-    const int len = pow2_ceil(k);
-    for (int i = k + threadIdx.x; i < len; i += blockDim.x) sh.buf[i] = 0;
-    __syncthreads();
-    bitonic_desc(sh.buf, len);
     for (int i = threadIdx.x; i < k; i += blockDim.x) {
         const uint64_t v = sh.buf[i];
-        topk_idx[m * k + i] = (int32_t)(~(uint32_t)v);
-        if (topk_val) topk_val[m * k + i] = key_score((uint32_t)(v >> 32));
+        int r = 0;
+        for (int j = 0; j < k; ++j) r += sh.buf[j] > v ? 1 : 0;
+        topk_idx[m * k + r] = (int32_t)(~(uint32_t)v);
+        if (topk_val) topk_val[m * k + r] = key_score((uint32_t)(v >> 32));
     }
 }
 
@@ -344,9 +353,12 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k)
     int64_t s = 1;
     while ((s * 2) * (s * 2) * 4 * (int64_t)k <= n && s * 2 <= nb) s *= 2;
     L.stride = s;
+    // per-lane maxima (one value per 32 or 16 tokens) carry almost the same
+    // tail information as the tokens themselves once there are >= 4k of them
+    L.lanemax = n >= 128 * (int64_t)k * s;
     L.cap = 8 * (int64_t)k * s + 1024;
     if (L.cap > nb * 64) L.cap = nb * 64;
-    L.sample_nlb = (nb + s - 1) / s;
+    L.sample_nlb = ((nb + 32 * s - 1) / (32 * s)) * 32;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     L.off_tau = 0;
     L.off_count = up((size_t)L.m * 4);
@@ -368,13 +380,15 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
     uint32_t* tau = (uint32_t*)(w + L.off_tau);
     uint32_t* counts = (uint32_t*)(w + L.off_count);
     uint64_t* cand = (uint64_t*)(w + L.off_cand);
-    const int64_t sblocks = (nb + L.stride - 1) / L.stride;
-    const int64_t last = (sblocks - 1) * L.stride;  // last sampled block
-    const int64_t valid = (sblocks - 1) * 64 + (n - last * 64 < 64 ? n - last * 64 : 64);
+    int64_t valid = 0;  // sampled tokens below n
+    for (int64_t b0 = 0; b0 < nb; b0 += 32 * L.stride) {
+        const int64_t lo = b0 * 64, hi = (b0 + 32) * 64 < n ? (b0 + 32) * 64 : n;
+        valid += hi - lo;
+    }
 
     fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
     threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, L.stride,
-                                                                 sblocks * 64, valid, k, tau);
+                                                                 L.sample_nlb * 64, valid, k, tau);
     filter_kernel<<<dim3((unsigned)L.m, (unsigned)((npad + 4095) / 4096)), 256, 0, st>>>(
         scores, n, npad, tau, counts, cand, L.cap);
     select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
@@ -395,7 +409,6 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
     uint32_t* flags = (uint32_t*)(w + L.off_flags);
     float* sample = (float*)(w + L.off_sample);
     float* repair = (float*)(w + L.off_repair);
-    const int64_t srow = L.sample_nlb * 64;
     hipError_t e;
     ScanArgs a = base;
 
@@ -406,9 +419,12 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         a.nlb = L.sample_nlb;
         a.out = sample;
         a.only = nullptr;
-        if ((e = launch_scan_args(a, P, G, false, st)) != hipSuccess) return e;
-        threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(sample, srow, srow, 1, srow,
-                                                                     srow, k, tau);
+        if ((e = launch_scan_args(a, P, G, L.lanemax ? 2 : 0, st)) != hipSuccess) return e;
+        // every lane maximum is a distinct token's score, so the k-th largest
+        // of them is still a lower bound of the k-th largest score
+        const int64_t row = L.sample_nlb * (L.lanemax ? (G <= 4 ? 2 : 4) : 64);
+        threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(sample, row, row, 1, row, row,
+                                                                     k, tau);
     }
     if (stages & 2) {
         // filter: every block, keeping the scores at or above the threshold
@@ -420,7 +436,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         a.cand = cand;
         a.cap = L.cap;
         a.only = nullptr;
-        if ((e = launch_scan_args(a, P, G, true, st)) != hipSuccess) return e;
+        if ((e = launch_scan_args(a, P, G, 1, st)) != hipSuccess) return e;
     }
     if (stages & 4) {
         // pairs whose candidates overflowed get their full scores recomputed
@@ -430,7 +446,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         a.nlb = nb;
         a.out = repair;
         a.only = flags;
-        if ((e = launch_scan_args(a, P, G, false, st)) != hipSuccess) return e;
+        if ((e = launch_scan_args(a, P, G, 0, st)) != hipSuccess) return e;
         // exact top-k of the candidates (or of the repaired scores), union
         select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(repair, n, npad, counts, cand,
                                                                   L.cap, k, topk_idx, topk_val);
