@@ -43,7 +43,23 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle beside it")
     ap.add_argument("--cpu-pairs", type=int, default=8)
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe(mib: int):
+    """A plain copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
 def src_hash(path: str) -> str:
@@ -85,15 +101,102 @@ def build_index(F, w, device):
 
 
 def inputs(w):
+    """Queries, and the calibration statistics: per-channel variances, or for
+    rotated storage the KLT basis and the variances of the rotated coordinates."""
     import workloads as wl
     from sparse_attention_key_amd import calib
 
     q = np.stack([wl.queries(w, p) for p in range(w.P)])
-    s2 = np.stack([calib.channel_variance(wl.calibration_sample(w, p)) for p in range(w.P)])
-    return q, s2
+    if not w.rotated:
+        s2 = np.stack([calib.channel_variance(wl.calibration_sample(w, p)) for p in range(w.P)])
+        return q, s2, None
+    rots, lams = zip(*(calib.rotation(wl.calibration_sample(w, p)) for p in range(w.P)))
+    return q, np.stack(lams), np.stack(rots)
 
 
-def cpu_baseline(w, q, s2, budget, mode, pairs, threads):
+def build_host_index(F, w, rot_np, device):
+    """Keys drawn on the GPU, rotated into the calibration basis (a float32
+    GEMM of the input generator side), packed on the GPU chunk by chunk and
+    copied into mapped pinned host memory."""
+    import torch
+
+    import workloads as wl
+
+    nb = w.nb
+    pbytes = w.D * 4 * nb * 8
+    sbytes = w.D * nb * 2
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    planes_h = PinnedHost(w.P * pbytes)
+    scales_h = PinnedHost(w.P * sbytes)
+    chunk = 8
+    stream = torch.cuda.current_stream()
+    planes = torch.empty((chunk, w.D, 4, nb), dtype=torch.int64, device=device)
+    scales = torch.empty((chunk, w.D, nb), dtype=torch.int16, device=device)
+    t0 = time.time()
+    for p0 in range(0, w.P, chunk):
+        pairs = list(range(p0, min(w.P, p0 + chunk)))
+        keys = wl.keys_device(w, pairs, device=device)
+        y = torch.empty((len(pairs), w.n, w.D), dtype=torch.float32, device=device)
+        for i, p in enumerate(pairs):
+            y[i] = keys[i].float() @ torch.from_numpy(rot_np[p]).to(device)
+        del keys
+        F.pack_into(y, planes[: len(pairs)], scales[: len(pairs)])
+        del y
+        planes_h.copy_from_device(p0 * pbytes, planes.data_ptr(), len(pairs) * pbytes, stream)
+        scales_h.copy_from_device(p0 * sbytes, scales.data_ptr(), len(pairs) * sbytes, stream)
+        torch.cuda.synchronize()
+        if (p0 // chunk) % 8 == 0:
+            log(f"packed pairs {p0}..{pairs[-1]} into pinned host memory ({time.time() - t0:.1f}s)")
+    del planes, scales
+    torch.cuda.empty_cache()
+    return planes_h, scales_h
+
+
+def link_probes(F, planes_h, device):
+    """Host-link read bandwidth: zero-copy streaming reads of the mapped
+    index, and pinned host-to-device hipMemcpy, over the same 4 GiB."""
+    import torch
+
+    nbytes = min(4 << 30, planes_h.nbytes)
+    sink = torch.zeros(1024, dtype=torch.int32, device=device)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("zero_copy_read", lambda: F.read_probe(planes_h.dev, nbytes, sink)),
+                     ("pinned_h2d_memcpy", lambda: planes_h.copy_to_device(dst.data_ptr(), 0, nbytes, stream))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(3 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+    del dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def hbm_probe(F, planes, device):
+    """Streaming read bandwidth of the HBM-resident index itself."""
+    import torch
+
+    nbytes = planes.numel() * 8
+    sink = torch.zeros(1024, dtype=torch.int32, device=device)
+    F.read_probe(planes, nbytes, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        F.read_probe(planes, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+
+def cpu_baseline(w, q, s2, budget, mode, pairs, threads, rot=None):
     """Time the CPU oracle (as it stands) on a bounded sample of pairs: the
     same plan + scores + top-k + union per pair, run `threads` pairs at a
     time; scaled to a whole step of all pairs."""
@@ -110,7 +213,10 @@ def cpu_baseline(w, q, s2, budget, mode, pairs, threads):
     torch.cuda.empty_cache()
 
     def prep(p):
-        packed[p] = oracle.pack(keys.pop(p))
+        x = keys.pop(p)
+        if rot is not None:
+            x = (x.astype(np.float64) @ rot[p].astype(np.float64)).astype(np.float32)
+        packed[p] = oracle.pack(x)
 
     with cf.ThreadPoolExecutor(max_workers=min(threads, pairs)) as ex:
         list(ex.map(prep, sel))
@@ -118,7 +224,8 @@ def cpu_baseline(w, q, s2, budget, mode, pairs, threads):
 
     def run(p):
         pl, sc = packed[p]
-        oracle.step(pl, sc, w.n, q[p], s2[p], budget, w.k, mode=mode)
+        oracle.step(pl, sc, w.n, q[p], s2[p], budget, w.k, mode=mode,
+                    rot=None if rot is None else rot[p])
 
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
@@ -136,6 +243,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the scan shards by "
               f"(layer, KV head) pair with no exchange, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
     import torch
 
     import workloads as wl
@@ -146,11 +256,22 @@ def main():
     dev = torch.device("cuda:0")
     F.lib()
     log(f"workload {w.name}: P={w.P} n={w.n} G={w.G} D={w.D} B={budget} k={w.k} mode={a.mode}")
-    q_np, s2_np = inputs(w)
+    q_np, s2_np, rot_np = inputs(w)
     log("calibration + queries ready")
-    planes, scales = build_index(F, w, dev)
+    host = None
+    link = {}
+    if w.host_resident:
+        host = build_host_index(F, w, rot_np, dev)
+        planes, scales = host[0].dev, host[1].dev  # device addresses of mapped host memory
+        link = link_probes(F, host[0], dev)
+        log(f"host link: {link}")
+    else:
+        planes, scales = build_index(F, w, dev)
+        link = {"hbm_read_probe": hbm_probe(F, planes, dev)}
+        log(f"HBM streaming read of the index: {link['hbm_read_probe']} GB/s")
     q = torch.from_numpy(q_np).to(dev)
     s2 = torch.from_numpy(s2_np).to(dev)
+    rot = None if rot_np is None else torch.from_numpy(rot_np).to(dev)
     pl = F.Plan(w.P, w.G, w.D, dev)
     npad = w.nb * 64
     out = F.TopkOut(w.P, w.G, w.n, w.k, dev, fused=True)
@@ -161,7 +282,7 @@ def main():
         """plan, then the three stages of the fused scan + top-k."""
         if rec is not None:
             rec[0].record()
-        F.plan_into(pl, q, s2, budget, a.mode)
+        F.plan_into(pl, q, s2, budget, a.mode, rot=rot)
         for s_ in (1, 2, 3):
             if rec is not None:
                 rec[s_].record()
@@ -190,7 +311,7 @@ def main():
     for r in [None] + mrec:
         if r is not None:
             r[0].record()
-        F.plan_into(pl, q, s2, budget, a.mode)
+        F.plan_into(pl, q, s2, budget, a.mode, rot=rot)
         F.scan_into(planes, scales, w.n, pl, scores)
         if r is not None:
             r[1].record()
@@ -214,6 +335,17 @@ def main():
         f"scan {scan_ms:.3f}, select {sel_ms:.3f}); scan {achieved:.0f} GB/s algorithmic; "
         f"bits/token {bits_tok:.2f}; materialised path {mat_total:.3f} ms (scan {mat_scan:.3f}), same={same}")
 
+    if host is None:
+        roof = {"bound": "hbm", "kernel": "scan_kernel (filter)", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(w.name), "alg_bytes_per_launch": alg_bytes,
+                "measured_read_probe_GBs": link["hbm_read_probe"]}
+    else:
+        peak = link["zero_copy_read"]
+        roof = {"bound": "host_link", "kernel": "scan_kernel (filter)", "achieved": round(achieved, 2),
+                "peak": peak, "peak_kind": "measured zero-copy read of the mapped index",
+                "unit": "GB/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "alg_bytes_per_launch": alg_bytes, "link_probes_GBs": link}
     res = {
         "metric": METRIC, "value": round(ms_step, 4), "unit": "ms/step", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
@@ -221,19 +353,22 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "pairs": w.P, "n": w.n, "G": w.G, "D": w.D, "budget": budget,
                    "mode": ["waterfill", "topr", "uniform"][a.mode], "k": w.k, "keys": w.key_dtype,
-                   "index": "hbm"},
+                   "index": "host-mapped pinned" if host else "hbm",
+                   "basis": "klt" if w.rotated else "raw"},
         "gpu_ms_per_step": round(gpu_ms, 4), "plan_ms": round(plan_ms, 4),
         "threshold_ms": round(thr_ms, 4), "scan_ms": round(scan_ms, 4), "select_ms": round(sel_ms, 4),
         "materialised_ms": round(mat_total, 4), "materialised_scan_ms": round(mat_scan, 4),
         "materialised_same_result": same,
         "keys_per_s": round(w.P * w.n / (ms_step * 1e-3), 1),
         "bits_per_token": round(bits_tok, 2), "active_channels_mean": round(float(act.double().mean()), 2),
-        "roofline": {"bound": "hbm", "kernel": "scan_kernel (filter)", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(w.name), "alg_bytes_per_launch": alg_bytes},
+        "roofline": roof,
     }
+    if host is not None:
+        for h in host:
+            h.free()
     if a.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, q_np, s2_np, budget, a.mode, a.cpu_pairs, a.cpu_threads)
+        res["cpu_baseline"] = cpu_baseline(w, q_np, s2_np, budget, a.mode, a.cpu_pairs, a.cpu_threads,
+                                           rot=rot_np)
     print(json.dumps(res), flush=True)
 
 

@@ -198,6 +198,16 @@ int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t
                            int32_t* topk_idx, float* topk_val, int32_t* union_idx,
                            int32_t* union_len, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * fathom_read_probe -- measurement utility, not a step of the method: reads
+ * `bytes` (rounded down to a multiple of 16) from `src` once with 16-byte
+ * coalesced loads and folds them into sink[0..1023] (caller-owned device
+ * memory, XOR-accumulated).  Timing it gives the read bandwidth the scan can
+ * reach on that memory: HBM, or the host link for a hipHostMalloc'd mapped
+ * buffer.  Errors: ERR_ARG (null, bytes < 16), ERR_ALIGN.
+ */
+int fathom_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

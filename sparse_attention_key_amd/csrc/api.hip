@@ -180,4 +180,11 @@ int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t
                           topk_val, union_idx, union_len, ws, ws_bytes, stream, 1 << (stage - 1));
 }
 
+int fathom_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream)
+{
+    if (!src || !sink || bytes < 16) return FATHOM_ERR_ARG;
+    if (!aligned16(src) || !aligned16(sink)) return FATHOM_ERR_ALIGN;
+    return hip_status(launch_read_probe(src, bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -130,6 +130,8 @@ struct ScanArgs {
 // mode: 0 store scores, 1 filter into candidates, 2 per-lane maxima
 hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream_t st);
 
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+
 struct TopkLayout {
     int64_t m;           // selections = P * G
     int64_t stride;      // sample one run of 32 blocks in every `stride` runs

@@ -232,12 +232,17 @@ __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ s
     const int64_t base = (int64_t)blockIdx.y * (256 * kItems);
     if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
+    float v[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {  // all loads in flight before any test
+        const int64_t tok = base + r * 256 + threadIdx.x;
+        v[r] = tok < n ? s[tok] : -INFINITY;
+    }
+#pragma unroll
     for (int r = 0; r < kItems; ++r) {
         const int64_t tok = base + r * 256 + threadIdx.x;
-        if (tok < n) {
-            const uint32_t key = score_key(s[tok]);
-            if (key >= th) s_c[atomicAdd(&s_n, 1u)] = composite(key, (uint32_t)tok);
-        }
+        const uint32_t key = score_key(v[r]);
+        if (tok < n && key >= th) s_c[atomicAdd(&s_n, 1u)] = composite(key, (uint32_t)tok);
     }
     __syncthreads();
     const uint32_t cnt = s_n;

@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.fathom_scan_topk_workspace_bytes.restype = sz
         L.fathom_scan_topk.argtypes = [P, P, i32, i32, i64, P, P, P, P, i32, i32, P, P, P, P, P, sz, P]
         L.fathom_scan_topk_stage.argtypes = [i32] + L.fathom_scan_topk.argtypes
+        L.fathom_read_probe.argtypes = [P, sz, P, P]
+        L.fathom_read_probe.restype = ctypes.c_int
         for f in (L.fathom_pack, L.fathom_plan, L.fathom_scan, L.fathom_topk, L.fathom_scan_topk,
                   L.fathom_scan_topk_stage):
             f.restype = ctypes.c_int
@@ -73,7 +75,13 @@ def _check(fn: str, rc: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor, or a raw address given as an int (e.g. a
+    mapped pinned host buffer)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream=None):
@@ -207,3 +215,8 @@ def scan_topk_stage(stage: int, planes, scales, n: int, pl: Plan, out: TopkOut, 
         _ptr(pl.n_active), _ptr(pl.q_used), pl.G, out.k, _ptr(out.idx), _ptr(out.val), _ptr(out.union),
         _ptr(out.union_len), _ptr(out.ws), out.ws.numel(), _stream(stream)))
     return out
+
+
+def read_probe(src, nbytes: int, sink, stream=None):
+    """Stream nbytes of src once (bandwidth probe; see fathom_read_probe)."""
+    _check("fathom_read_probe", lib().fathom_read_probe(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)))

@@ -300,3 +300,39 @@ def test_fused_scan_topk_bit_exact(F, orc, kind, n, D, G, budget, k, mode):
             assert np.array_equal(val[p, h], ref["scores"][h][ref["topk"][h]])
         assert int(out.union_len[p]) == ref["union_len"]
         assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+
+
+def test_host_resident_index_matches_device(F, orc):
+    """The scan reads a mapped pinned host copy of the index over the host
+    link and must give the same bits as from HBM (KLT-rotated storage)."""
+    import torch
+
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    w = wl.WORKLOADS["host1m_klt"]
+    P, n = 2, 40000 + 11
+    xs = [wl.keys_host(w, p, n=n) for p in range(P)]
+    qs = np.stack([wl.queries(w, p) for p in range(P)])
+    rots, lams = zip(*[orc.calib.klt_basis(wl.calibration_sample(w, p)) for p in range(P)])
+    rot, lam = np.stack(rots), np.stack(lams)
+    say("host-resident index", n)
+    planes, scales = F.pack(bf16_dev(np.stack(xs)), rot=dev(rot))
+    ph = PinnedHost(planes.numel() * 8)
+    sh = PinnedHost(scales.numel() * 2)
+    st = torch.cuda.current_stream()
+    ph.copy_from_device(0, planes.data_ptr(), planes.numel() * 8, st)
+    sh.copy_from_device(0, scales.data_ptr(), scales.numel() * 2, st)
+    torch.cuda.synchronize()
+    pl = F.plan(dev(qs), dev(lam), w.budget, 0, rot=dev(rot))
+    ref = F.scan_topk(planes, scales, n, pl, w.k)
+    got = F.scan_topk(ph.dev, sh.dev, n, pl, w.k)
+    s_dev = F.scan(planes, scales, n, pl)
+    s_host = F.scan(ph.dev, sh.dev, n, pl)
+    torch.cuda.synchronize()
+    assert torch.equal(s_dev, s_host)
+    assert torch.equal(ref.idx, got.idx) and torch.equal(ref.union, got.union)
+    for p in range(P):
+        _compare_pair(orc, p, xs[p], qs[p], lam[p], w.budget, w.k, n, pl, s_host, got,
+                      rot=rot[p], keys_rot=rot[p])
+    ph.free()
+    sh.free()
