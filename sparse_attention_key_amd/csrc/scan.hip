@@ -85,6 +85,57 @@ __device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, 
     }
 }
 
+// Plane words and scale of one channel for one lane, loaded ahead of use.
+// Loads are buffer loads: the channel's row base lives in an SGPR resource
+// descriptor and the lane adds a small byte offset, so no per-lane 64-bit
+// address arithmetic is spent.  Every channel issues exactly five loads --
+// absent planes re-read plane 0, a cache hit that costs no HBM bytes -- so
+// the number of loads in flight is static and the waits are exact.
+template <class WT>
+struct ChanWords {
+    uint32_t w0, w1, w2, w3, sc;
+
+    __device__ __forceinline__ void issue(const uint64_t* pplanes, const uint16_t* pscales,
+                                          int64_t nb, uint32_t loff, uint32_t soff, int jt_lds)
+    {
+        const int jt = __builtin_amdgcn_readfirstlane(jt_lds);
+        const int j = jt & 0xFFFF, t = jt >> 16;
+        const int row = (int)(nb * 8);
+        __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(pplanes + (size_t)j * 4 * nb), (short)0, 4 * row, 0x00020000);
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(pscales + (size_t)j * nb), (short)0, (int)(nb * 2), 0x00020000);
+        if (sizeof(WT) == 4) {
+            w0 = __builtin_amdgcn_raw_buffer_load_b32(rp, loff, 0, 0);
+            w1 = __builtin_amdgcn_raw_buffer_load_b32(rp, loff, t > 1 ? row : 0, 0);
+            w2 = __builtin_amdgcn_raw_buffer_load_b32(rp, loff, t > 2 ? 2 * row : 0, 0);
+            w3 = __builtin_amdgcn_raw_buffer_load_b32(rp, loff, t > 3 ? 3 * row : 0, 0);
+        } else {
+            w0 = __builtin_amdgcn_raw_buffer_load_b16(rp, loff, 0, 0);
+            w1 = __builtin_amdgcn_raw_buffer_load_b16(rp, loff, t > 1 ? row : 0, 0);
+            w2 = __builtin_amdgcn_raw_buffer_load_b16(rp, loff, t > 2 ? 2 * row : 0, 0);
+            w3 = __builtin_amdgcn_raw_buffer_load_b16(rp, loff, t > 3 ? 3 * row : 0, 0);
+        }
+        sc = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, 0, 0);
+    }
+
+    template <int G, int TOK>
+    __device__ __forceinline__ void consume(int jt_lds, const float (&q)[G], float (&acc)[TOK][G]) const
+    {
+        const int t = __builtin_amdgcn_readfirstlane(jt_lds) >> 16;
+        float qv[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) qv[h] = q[h];
+        const uint32_t w[4] = {w0, w1, w2, w3};  // planes >= t are not read by codes()
+        const float scf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc);  // v_cvt_f32_f16, exact
+        const float delta = scf * 0.125f;
+        const float c0 = scf * __uint_as_float((uint32_t)(127 - t) << 23) * (float)(1 - (1 << t));
+        uint32_t c[8];
+        codes<TOK>(w, t, c);
+        accumulate<G, TOK>(c, delta, c0, qv, acc);
+    }
+};
+
 enum { kStore = 0, kFilter = 1, kLaneMax = 2 };
 
 template <int G, int TOK, int MODE>
@@ -121,9 +172,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     const bool live = lb < a.nlb && phys < a.nb;
     const int64_t blk = live ? phys : 0;
     const int64_t nb = a.nb;
-    const WT* pw = reinterpret_cast<const WT*>(a.planes + (size_t)p * a.D * 4 * nb + blk) + part;
-    const uint16_t* ps = a.scales + (size_t)p * a.D * nb + blk;
-    constexpr int kWordStride = 8 / sizeof(WT);  // WT elements per 64-bit plane word
+    const uint64_t* pplanes = a.planes + (size_t)p * a.D * 4 * nb;  // uniform
+    const uint16_t* pscales = a.scales + (size_t)p * a.D * nb;
+    const uint32_t loff = (uint32_t)(blk * 8 + part * (int)sizeof(WT));
+    const uint32_t soff = (uint32_t)(blk * 2);
 
     float acc[TOK][G];
 #pragma unroll
@@ -131,44 +183,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
 #pragma unroll
         for (int h = 0; h < G; ++h) acc[i][h] = 0.0f;
 
-    // software pipeline: words and scale of channel e+1 load during channel e
-    uint32_t wn0 = 0, wn1 = 0, wn2 = 0, wn3 = 0, scn = 0;
-    int jtn = 0;
+    // two register sets in ping-pong: the next channel's loads are in flight
+    // while the current one is accumulated, with no register copies
     if (A > 0) {
-        jtn = s_jt[0];
-        const int j = jtn & 0xFFFF, t = jtn >> 16;
-        const WT* src = pw + (size_t)j * 4 * nb * kWordStride;
-        const size_t ps_ = (size_t)nb * kWordStride;
-        wn0 = src[0];
-        wn1 = t > 1 ? (uint32_t)src[ps_] : 0u;
-        wn2 = t > 2 ? (uint32_t)src[2 * ps_] : 0u;
-        wn3 = t > 3 ? (uint32_t)src[3 * ps_] : 0u;
-        scn = ps[(size_t)j * nb];
-    }
-    for (int e = 0; e < A; ++e) {
-        const uint32_t w[4] = {wn0, wn1, wn2, wn3};
-        const uint32_t sc = scn;
-        const int t = jtn >> 16;
-        float qv[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) qv[h] = s_q[e][h];
-        if (e + 1 < A) {
-            jtn = s_jt[e + 1];
-            const int j = jtn & 0xFFFF, tn = jtn >> 16;
-            const WT* src = pw + (size_t)j * 4 * nb * kWordStride;
-            const size_t ps_ = (size_t)nb * kWordStride;
-            wn0 = src[0];
-            wn1 = tn > 1 ? (uint32_t)src[ps_] : 0u;
-            wn2 = tn > 2 ? (uint32_t)src[2 * ps_] : 0u;
-            wn3 = tn > 3 ? (uint32_t)src[3 * ps_] : 0u;
-            scn = ps[(size_t)j * nb];
+        ChanWords<WT> X, Y;
+        X.issue(pplanes, pscales, nb, loff, soff, s_jt[0]);
+        for (int e = 0; e < A; e += 2) {
+            Y.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 1 < A ? e + 1 : A - 1]);
+            X.template consume<G, TOK>(s_jt[e], s_q[e], acc);
+            X.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 2 < A ? e + 2 : A - 1]);
+            if (e + 1 < A) Y.template consume<G, TOK>(s_jt[e + 1], s_q[e + 1], acc);
         }
-        const float scf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc);  // v_cvt_f32_f16, exact
-        const float delta = scf * 0.125f;
-        const float c0 = scf * __uint_as_float((uint32_t)(127 - t) << 23) * (float)(1 - (1 << t));
-        uint32_t c[8];
-        codes<TOK>(w, t, c);
-        accumulate<G, TOK>(c, delta, c0, qv, acc);
     }
 
     const int64_t tok0 = blk * 64 + part * TOK;   // physical token of acc[0]
