@@ -26,6 +26,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scan+top-k ms/decode step at 1M tokens; achieved GB/s vs HBM peak"
 HBM_PEAK_GBS = 8000.0
+# fp32 vector peak: 256 CUs x 64 lanes x 2.4 GHz x 2 FLOP per FMA x 2 (packed
+# dual FMA).  Without packed fp32 a lane retires one FMA per cycle: half that.
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9
 
 
 def log(*a):
@@ -66,16 +70,16 @@ def src_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per scan launch from committed rocprofv3 counters, if they
-    were taken on the current scan source; otherwise None."""
+def scan_counters(workload: str) -> dict:
+    """Committed rocprofv3 counters of the filtered scan (HBM bytes per launch,
+    VALU activity), if they were taken on the current scan source; else {}."""
     f = os.path.join(ROOT, "profiles", f"scan_{workload}_pmc.json")
     if not os.path.exists(f):
-        return None
+        return {}
     d = json.load(open(f))
     if d.get("scan_src_sha256_16") != src_hash(os.path.join(ROOT, "sparse_attention_key_amd", "csrc", "scan.hip")):
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return {}
+    return d
 
 
 def build_index(F, w, device):
@@ -194,6 +198,44 @@ def hbm_probe(F, planes, device):
     e1.record()
     torch.cuda.synchronize()
     return round(5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+
+def fetch_probe(F, w, out, device):
+    """Winner-row fetch after the step: the union rows of every pair (K and V
+    of one token side by side, bf16, D=128 each: 512 B) gathered from a
+    row table in mapped pinned host memory into HBM.  One table of n rows is
+    shared by all pairs (the link carries the same bytes as per-pair tables,
+    without 151 GB of pinned memory)."""
+    import torch
+
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    row_bytes = 2 * w.D * 2
+    nbytes = w.n * row_bytes
+    src = torch.randint(-32768, 32767, (nbytes // 2,), dtype=torch.int16, device=device)
+    table = PinnedHost(nbytes)
+    table.copy_from_device(0, src.data_ptr(), nbytes, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    del src
+    cap = out.union.shape[1]
+    dst = torch.empty((w.P, cap, row_bytes // 2), dtype=torch.int16, device=device)
+    F.gather_rows(table.dev, w.n, row_bytes, 0, out.union, out.union_len, dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        F.gather_rows(table.dev, w.n, row_bytes, 0, out.union, out.union_len, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    rows = int(out.union_len.to(torch.int64).sum().item())
+    table.free()
+    del dst
+    torch.cuda.empty_cache()
+    return {"rows": rows, "bytes": rows * row_bytes, "ms": round(ms, 4),
+            "GBps": round(rows * row_bytes / (ms * 1e-3) / 1e9, 2),
+            "source": "mapped pinned host memory, K|V rows of 512 B (bf16, D=128)"}
 
 
 def cpu_baseline(w, q, s2, budget, mode, pairs, threads, rot=None):
@@ -336,10 +378,26 @@ def main():
         f"bits/token {bits_tok:.2f}; materialised path {mat_total:.3f} ms (scan {mat_scan:.3f}), same={same}")
 
     if host is None:
-        roof = {"bound": "hbm", "kernel": "scan_kernel (filter)", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(w.name), "alg_bytes_per_launch": alg_bytes,
-                "measured_read_probe_GBs": link["hbm_read_probe"]}
+        # The HBM-resident scan is bound by plain fp32 VALU arithmetic: rocprofv3
+        # shows the VALU busy nearly every cycle while HBM runs far below its
+        # rate.  Algorithmic work: 2*G FLOP per (token, active channel).
+        elems = int(act.sum().item()) * w.n
+        alg_flops = 2 * w.G * elems
+        tflops = alg_flops / (scan_ms * 1e-3) / 1e12
+        prof = scan_counters(w.name)
+        ops = prof.get("valu_lane_ops_per_elem")
+        roof = {"bound": "alu", "kernel": "scan_kernel (filter)", "achieved": round(tflops, 2),
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+                "traffic": prof.get("hbm_bytes_per_launch"), "alg_flops_per_launch": alg_flops,
+                "peak_without_packed_fp32": FP32_VECTOR_PEAK_TFLOPS / 2,
+                "valu_busy": prof.get("valu_busy"), "valu_lane_ops_per_elem": ops,
+                "hbm": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes,
+                        "measured_read_probe_GBs": link["hbm_read_probe"],
+                        # the rate the VALU allows at the measured instruction count
+                        "valu_ceiling_GBs": (round(VALU_LANE_OPS_PER_S / ops * alg_bytes / elems / 1e9, 1)
+                                             if ops else None)}}
     else:
         peak = link["zero_copy_read"]
         roof = {"bound": "host_link", "kernel": "scan_kernel (filter)", "achieved": round(achieved, 2),
@@ -366,6 +424,9 @@ def main():
     if host is not None:
         for h in host:
             h.free()
+    if w.n >= (1 << 17):
+        res["fetch"] = fetch_probe(F, w, out, dev)
+        log(f"winner-row fetch: {res['fetch']}")
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q_np, s2_np, budget, a.mode, a.cpu_pairs, a.cpu_threads,
                                            rot=rot_np)

@@ -12,8 +12,9 @@
  * head plus their union per KV head.
  *
  * Conventions shared by every entry point
- *  - A "pair" is one (layer, KV head).  P pairs are processed per call; every
- *    array below is pair-major and densely packed.
+ *  - A "pair" is one (layer, KV head).  P pairs (1 <= P <= FATHOM_MAX_PAIRS)
+ *    are processed per call; every array below is pair-major and densely
+ *    packed.
  *  - All pointers are DEVICE pointers (hipMalloc'd, or host memory mapped
  *    into the device address space with hipHostMalloc(..., Mapped) -- the
  *    scan reads such an index over the host link), owned by the caller, and
@@ -63,6 +64,7 @@ extern "C" {
 #define FATHOM_PLAN_UNIFORM 2   /* budget = depth of every channel (0..4)           */
 
 #define FATHOM_MAX_K 4096
+#define FATHOM_MAX_PAIRS 65535 /* P per call (pairs run on the grid's y axis) */
 
 int fathom_abi_version(void);
 const char* fathom_strerror(int status);
@@ -197,6 +199,28 @@ int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t
                            const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
                            int32_t* topk_idx, float* topk_val, int32_t* union_idx,
                            int32_t* union_len, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fathom_gather_rows -- the winner-row fetch that follows the selection:
+ * copy the union rows of every pair (the keys and values a decode step
+ * attends to, at most G*k rows per KV head) out of a row table that may live
+ * in mapped host memory (byte-accounting and experiments sections).
+ *
+ *   table      row-major table of table_rows rows of row_bytes bytes per pair
+ *              (e.g. K and V of one token side by side: 2 * D * 2 bytes in
+ *              bf16); pair p's token i is row p * pair_stride_rows + i, so
+ *              pair_stride_rows = table_rows gives one table per pair and 0
+ *              one table shared by all pairs
+ *   union_idx  [P][cap] int32 ascending token indices (fathom_topk's union)
+ *   union_len  [P]      int32 rows to fetch per pair (<= cap)
+ *   out        [P][cap][row_bytes] device memory; rows r >= union_len[p] and
+ *              indices outside [0, table_rows) are left untouched
+ * row_bytes must be a positive multiple of 16 and 1 <= P <= FATHOM_MAX_PAIRS.  All
+ * pointers 16-byte aligned.  Errors: ERR_ARG (null), ERR_SHAPE, ERR_ALIGN.
+ */
+int fathom_gather_rows(const void* table, int64_t table_rows, int64_t row_bytes,
+                       int64_t pair_stride_rows, int32_t P, const int32_t* union_idx,
+                       const int32_t* union_len, int32_t cap, void* out, void* stream);
 
 /*
  * fathom_read_probe -- measurement utility, not a step of the method: reads

@@ -224,5 +224,19 @@ def step(planes, scales, n, q, sigma2, budget, k, mode=PLAN_WATERFILL, rot=None)
     return dict(depth=depth, q_used=q_used, scores=scores, topk=tk, union=un, union_len=int(ln))
 
 
+def gather_rows(table: np.ndarray, union_idx: np.ndarray, union_len: np.ndarray, out: np.ndarray):
+    """Winner-row fetch by definition: out[p][r] = table[p][union_idx[p][r]]
+    for r < union_len[p] and valid indices (table [P][rows][...] or a shared
+    [rows][...] table); other rows of `out` are left as they are."""
+    out = out.copy()
+    for p in range(union_idx.shape[0]):
+        t = table if table.ndim == out.ndim - 1 else table[p]
+        for r in range(int(union_len[p])):
+            i = int(union_idx[p, r])
+            if 0 <= i < t.shape[0]:
+                out[p, r] = t[i]
+    return out
+
+
 from . import ref64  # noqa: E402,F401  (float64 definitions)
 from . import calib  # noqa: E402,F401  (calibration statistics)

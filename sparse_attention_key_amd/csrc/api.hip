@@ -13,7 +13,7 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? FATHOM_OK : FATHO
 
 inline int check_shape(int32_t P, int64_t n, int32_t D)
 {
-    if (P < 1 || n < 1 || D < 1 || D > kMaxD) return FATHOM_ERR_SHAPE;
+    if (P < 1 || P > kMaxPairs || n < 1 || D < 1 || D > kMaxD) return FATHOM_ERR_SHAPE;
     if (n > ((int64_t)1 << 31) - 64) return FATHOM_ERR_SHAPE;  // token index fits int32
     return FATHOM_OK;
 }
@@ -178,6 +178,24 @@ int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t
     if (stage < 1 || stage > 3) return FATHOM_ERR_ARG;
     return scan_topk_impl(planes, scales, P, D, n, depth, active, n_active, q_used, G, k, topk_idx,
                           topk_val, union_idx, union_len, ws, ws_bytes, stream, 1 << (stage - 1));
+}
+
+int fathom_gather_rows(const void* table, int64_t table_rows, int64_t row_bytes,
+                       int64_t pair_stride_rows, int32_t P, const int32_t* union_idx,
+                       const int32_t* union_len, int32_t cap, void* out, void* stream)
+{
+    if (!table || !union_idx || !union_len || !out) return FATHOM_ERR_ARG;
+    if (P < 1 || cap < 1 || table_rows < 1 || row_bytes < 16 || row_bytes % 16 != 0 ||
+        pair_stride_rows < 0)
+        return FATHOM_ERR_SHAPE;
+    if (pair_stride_rows != 0 && pair_stride_rows < table_rows) return FATHOM_ERR_SHAPE;
+    // pairs run on grid.y; the pieces of one pair's rows on grid.x
+    if (P > kMaxPairs || (int64_t)cap * (row_bytes / 16) > ((int64_t)1 << 40)) return FATHOM_ERR_SHAPE;
+    const void* ps[] = {table, union_idx, union_len, out};
+    for (const void* p : ps)
+        if (!aligned16(p)) return FATHOM_ERR_ALIGN;
+    return hip_status(launch_gather(table, table_rows, row_bytes, pair_stride_rows, P, union_idx,
+                                    union_len, cap, out, (hipStream_t)stream));
 }
 
 int fathom_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream)

@@ -12,6 +12,7 @@ constexpr int kWave = 64;
 constexpr int kMaxD = 128;
 constexpr int kMaxG = 8;
 constexpr int kMaxK = 4096;
+constexpr int kMaxPairs = 65535;  // P per call: pairs run on grid.y
 constexpr int kMaxUnion = 16384;  // G * k handled by the union kernel
 
 // ---------------------------------------------------------------- numerics
@@ -130,6 +131,9 @@ struct ScanArgs {
 // mode: 0 store scores, 1 filter into candidates, 2 per-lane maxima
 hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream_t st);
 
+hipError_t launch_gather(const void* table, int64_t table_rows, int64_t row_bytes,
+                         int64_t pair_stride, int P, const int32_t* idx, const int32_t* len,
+                         int cap, void* out, hipStream_t st);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 
 struct TopkLayout {

@@ -229,29 +229,34 @@ __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ s
     const int64_t m = blockIdx.x;
     const uint32_t th = tau[m];
     const float* s = scores + m * npad;
-    const int64_t base = (int64_t)blockIdx.y * (256 * kItems);
-    if (threadIdx.x == 0) s_n = 0;
-    __syncthreads();
-    float v[kItems];
+    const int64_t chunks = (npad + 256 * kItems - 1) / (256 * kItems);
+    for (int64_t c = blockIdx.y; c < chunks; c += gridDim.y) {
+        const int64_t base = c * (256 * kItems);
+        if (threadIdx.x == 0) s_n = 0;
+        __syncthreads();
+        float v[kItems];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {  // all loads in flight before any test
-        const int64_t tok = base + r * 256 + threadIdx.x;
-        v[r] = tok < n ? s[tok] : -INFINITY;
-    }
+        for (int r = 0; r < kItems; ++r) {  // all loads in flight before any test
+            const int64_t tok = base + r * 256 + threadIdx.x;
+            v[r] = tok < n ? s[tok] : -INFINITY;
+        }
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
-        const int64_t tok = base + r * 256 + threadIdx.x;
-        const uint32_t key = score_key(v[r]);
-        if (tok < n && key >= th) s_c[atomicAdd(&s_n, 1u)] = composite(key, (uint32_t)tok);
+        for (int r = 0; r < kItems; ++r) {
+            const int64_t tok = base + r * 256 + threadIdx.x;
+            const uint32_t key = score_key(v[r]);
+            if (tok < n && key >= th) s_c[atomicAdd(&s_n, 1u)] = composite(key, (uint32_t)tok);
+        }
+        __syncthreads();
+        const uint32_t cnt = s_n;  // uniform over the workgroup
+        if (cnt != 0) {
+            if (threadIdx.x == 0) s_base = atomicAdd(&counts[m], cnt);
+            __syncthreads();
+            const int64_t b0 = s_base;
+            for (uint32_t i = threadIdx.x; i < cnt; i += 256)
+                if (b0 + i < cap) cand[m * cap + b0 + i] = s_c[i];
+        }
+        __syncthreads();  // s_c, s_n and s_base are reused by the next chunk
     }
-    __syncthreads();
-    const uint32_t cnt = s_n;
-    if (cnt == 0) return;
-    if (threadIdx.x == 0) s_base = atomicAdd(&counts[m], cnt);
-    __syncthreads();
-    const int64_t b0 = s_base;
-    for (uint32_t i = threadIdx.x; i < cnt; i += 256)
-        if (b0 + i < cap) cand[m * cap + b0 + i] = s_c[i];
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
@@ -394,8 +399,16 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
     fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
     threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, L.stride,
                                                                  L.sample_nlb * 64, valid, k, tau);
-    filter_kernel<<<dim3((unsigned)L.m, (unsigned)((npad + 4095) / 4096)), 256, 0, st>>>(
-        scores, n, npad, tau, counts, cand, L.cap);
+    {
+        // chunks of 4096 scores on grid.y, looped inside once there are more
+        // than enough workgroups to fill the chip (grid.y stays below 65536)
+        const int64_t chunks = (npad + 4095) / 4096;
+        int64_t gy = (16384 + L.m - 1) / L.m;
+        gy = gy < 64 ? 64 : gy > 65535 ? 65535 : gy;
+        gy = gy < chunks ? gy : chunks;
+        filter_kernel<<<dim3((unsigned)L.m, (unsigned)gy), 256, 0, st>>>(scores, n, npad, tau,
+                                                                           counts, cand, L.cap);
+    }
     select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
                                                               k, topk_idx, topk_val);
     union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(topk_idx, G, k, union_idx, union_len);

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.fathom_scan_topk.argtypes = [P, P, i32, i32, i64, P, P, P, P, i32, i32, P, P, P, P, P, sz, P]
         L.fathom_scan_topk_stage.argtypes = [i32] + L.fathom_scan_topk.argtypes
         L.fathom_read_probe.argtypes = [P, sz, P, P]
+        L.fathom_gather_rows.argtypes = [P, i64, i64, i64, i32, P, P, i32, P, P]
+        L.fathom_gather_rows.restype = ctypes.c_int
         L.fathom_read_probe.restype = ctypes.c_int
         for f in (L.fathom_pack, L.fathom_plan, L.fathom_scan, L.fathom_topk, L.fathom_scan_topk,
                   L.fathom_scan_topk_stage):
@@ -220,3 +222,14 @@ def scan_topk_stage(stage: int, planes, scales, n: int, pl: Plan, out: TopkOut, 
 def read_probe(src, nbytes: int, sink, stream=None):
     """Stream nbytes of src once (bandwidth probe; see fathom_read_probe)."""
     _check("fathom_read_probe", lib().fathom_read_probe(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)))
+
+
+def gather_rows(table, table_rows: int, row_bytes: int, pair_stride_rows: int, union, union_len, out,
+                stream=None):
+    """Fetch the union rows of every pair from a row table (device memory or
+    mapped host memory given as an int address) into out [P][cap][row_bytes]."""
+    P, cap = union.shape
+    _check("fathom_gather_rows", lib().fathom_gather_rows(
+        _ptr(table), int(table_rows), int(row_bytes), int(pair_stride_rows), P, _ptr(union),
+        _ptr(union_len), cap, _ptr(out), _stream(stream)))
+    return out

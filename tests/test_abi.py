@@ -37,6 +37,7 @@ def test_pack_validation(L):
     assert L.fathom_pack(A, 0, 1, 0, 128, None, A, A, None) == F.ERR_SHAPE
     assert L.fathom_pack(A, 0, 1, 64, 129, None, A, A, None) == F.ERR_SHAPE
     assert L.fathom_pack(A, 0, 1, 1 << 31, 128, None, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_pack(A, 0, 65536, 64, 128, None, A, A, None) == F.ERR_SHAPE
     assert L.fathom_pack(MIS, 0, 1, 64, 128, None, A, A, None) == F.ERR_ALIGN
     assert L.fathom_pack(A, 1, 1, 64, 128, MIS, A, A, None) == F.ERR_ALIGN
 
@@ -69,6 +70,9 @@ def test_scan_validation(L):
     bad[4] = 0
     assert L.fathom_scan(*bad) == F.ERR_SHAPE
     bad = list(base)
+    bad[2] = 65536
+    assert L.fathom_scan(*bad) == F.ERR_SHAPE
+    bad = list(base)
     bad[0] = MIS
     assert L.fathom_scan(*bad) == F.ERR_ALIGN
 
@@ -95,3 +99,18 @@ def test_workspace_scales_with_sample_stride(L):
     # the 4.8 GB a full score copy would need
     b = L.fathom_topk_workspace_bytes(288, 4, 1 << 20, 512)
     assert 0 < b < 1 << 30
+
+
+def test_gather_validation(L):
+    args = lambda **kw: [kw.get("t", A), kw.get("rows", 1000), kw.get("rb", 512), kw.get("ps", 1000), 2,
+                         A, A, kw.get("cap", 64), kw.get("out", A), None]
+    assert L.fathom_gather_rows(*args(t=None)) == F.ERR_ARG
+    assert L.fathom_gather_rows(*args(out=None)) == F.ERR_ARG
+    assert L.fathom_gather_rows(*args(rb=500)) == F.ERR_SHAPE
+    assert L.fathom_gather_rows(*args(rb=0)) == F.ERR_SHAPE
+    assert L.fathom_gather_rows(*args(cap=0)) == F.ERR_SHAPE
+    assert L.fathom_gather_rows(*args(ps=999)) == F.ERR_SHAPE
+    ok = args()
+    ok[4] = 65536
+    assert L.fathom_gather_rows(*ok) == F.ERR_SHAPE
+    assert L.fathom_gather_rows(*args(t=MIS)) == F.ERR_ALIGN

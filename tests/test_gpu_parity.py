@@ -336,3 +336,39 @@ def test_host_resident_index_matches_device(F, orc):
                       rot=rot[p], keys_rot=rot[p])
     ph.free()
     sh.free()
+
+
+@pytest.mark.parametrize("shared,host", [(False, False), (True, False), (False, True), (True, True)])
+def test_gather_rows_bit_exact(F, orc, shared, host):
+    """Winner-row fetch: union rows of every pair copied out of a K|V row
+    table in HBM or in mapped pinned host memory."""
+    import torch
+
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    P, rows, row_bytes, cap = 3, 5000, 512, 700
+    g = np.random.default_rng(11 + shared + 2 * host)
+    shape = (rows, row_bytes // 2) if shared else (P, rows, row_bytes // 2)
+    table = g.integers(0, 65536, shape, dtype=np.uint16)
+    idx = np.full((P, cap), -1, np.int32)
+    lens = np.array([0, 357, cap], np.int32)
+    for p in range(P):
+        idx[p, :lens[p]] = np.sort(g.choice(rows, lens[p], replace=False))
+    idx[2, 5] = rows + 3  # an index outside the table is skipped
+    say("gather", shared, host)
+    tdev = torch.from_numpy(table.view(np.int16)).cuda()
+    src = tdev
+    ph = None
+    if host:
+        ph = PinnedHost(table.nbytes)
+        ph.copy_from_device(0, tdev.data_ptr(), table.nbytes, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        src = ph.dev
+    init = g.integers(0, 65536, (P, cap, row_bytes // 2), dtype=np.uint16)
+    out = torch.from_numpy(init.view(np.int16)).cuda()
+    F.gather_rows(src, rows, row_bytes, 0 if shared else rows, dev(idx), dev(lens), out)
+    got = out.cpu().numpy().view(np.uint16)
+    ref = orc.gather_rows(table, idx, lens, init)
+    assert np.array_equal(got, ref)
+    if ph is not None:
+        ph.free()

@@ -404,3 +404,18 @@ def test_tiny_planted_keys_win(orc):
     for h in range(w.G):
         assert set(pos[h]) <= set(out["topk"][h])
     assert out["union_len"] <= w.G * w.k
+
+
+def test_gather_rows_definition(orc):
+    # identity indices return the table's leading rows; a shared table equals
+    # the same table replicated per pair; rows past the length stay untouched
+    g = np.random.default_rng(60)
+    table = g.integers(0, 1000, (50, 4))
+    idx = np.tile(np.arange(10, dtype=np.int32), (2, 1))
+    lens = np.array([10, 4], np.int32)
+    init = -np.ones((2, 10, 4), np.int64)
+    out = orc.gather_rows(table, idx, lens, init)
+    assert np.array_equal(out[0], table[:10])
+    assert np.array_equal(out[1, :4], table[:4]) and np.all(out[1, 4:] == -1)
+    rep = orc.gather_rows(np.stack([table, table]), idx, lens, init)
+    assert np.array_equal(out, rep)
