@@ -71,7 +71,7 @@ __device__ __forceinline__ void codes(const uint32_t (&w)[4], int t, uint32_t (&
 // exact dequantised prefix (delta = scale/8, c0 = (1 - 2^t) * 2^-t * scale).
 template <int G, int TOK>
 __device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, float c0,
-                                           const float (&qv)[G], float (&acc)[TOK][G])
+                                           const float (&qv)[G], float (&acc)[G][TOK])
 {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -80,7 +80,7 @@ __device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, 
             const float cf = (float)((c[g] >> (8 * b)) & 0xFFu);
             const float kh = __builtin_fmaf(cf, delta, c0);  // exact
 #pragma unroll
-            for (int h = 0; h < G; ++h) acc[g + 8 * b][h] = __builtin_fmaf(qv[h], kh, acc[g + 8 * b][h]);
+            for (int h = 0; h < G; ++h) acc[h][g + 8 * b] = __builtin_fmaf(qv[h], kh, acc[h][g + 8 * b]);
         }
     }
 }
@@ -120,7 +120,7 @@ struct ChanWords {
     }
 
     template <int G, int TOK>
-    __device__ __forceinline__ void consume(int jt_lds, const float (&q)[G], float (&acc)[TOK][G]) const
+    __device__ __forceinline__ void consume(int jt_lds, const float (&q)[G], float (&acc)[G][TOK]) const
     {
         const int t = __builtin_amdgcn_readfirstlane(jt_lds) >> 16;
         float qv[G];
@@ -148,6 +148,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     __shared__ float s_q[kMaxD][G];
     constexpr bool FILTER = MODE == kFilter;
     __shared__ __attribute__((aligned(16))) float s_stage[FILTER ? kScanThreads / kWave : 1][kWave][TOK + 4];
+    __shared__ uint32_t s_wcount[kScanThreads / kWave][G];
 
     const int p = blockIdx.y;
     if (a.only && a.only[p] == 0) return;
@@ -177,22 +178,38 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     const uint32_t loff = (uint32_t)(blk * 8 + part * (int)sizeof(WT));
     const uint32_t soff = (uint32_t)(blk * 2);
 
-    float acc[TOK][G];
+    float acc[G][TOK];  // head-major: acc[h][i..i+3] are four consecutive registers
 #pragma unroll
-    for (int i = 0; i < TOK; ++i)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[i][h] = 0.0f;
+        for (int i = 0; i < TOK; ++i) acc[h][i] = 0.0f;
 
-    // two register sets in ping-pong: the next channel's loads are in flight
-    // while the current one is accumulated, with no register copies
+    // register sets in rotation, with no copies: while one channel is
+    // accumulated the loads of the next two (one for G = 8, whose extra
+    // accumulators leave no room for a third set) are in flight.  Indices
+    // past the end re-issue the last channel: cache hits that nobody reads.
     if (A > 0) {
+        const int last = A - 1;
         ChanWords<WT> X, Y;
         X.issue(pplanes, pscales, nb, loff, soff, s_jt[0]);
-        for (int e = 0; e < A; e += 2) {
-            Y.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 1 < A ? e + 1 : A - 1]);
-            X.template consume<G, TOK>(s_jt[e], s_q[e], acc);
-            X.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 2 < A ? e + 2 : A - 1]);
-            if (e + 1 < A) Y.template consume<G, TOK>(s_jt[e + 1], s_q[e + 1], acc);
+        if (G < 8) {
+            ChanWords<WT> Z;
+            Y.issue(pplanes, pscales, nb, loff, soff, s_jt[1 < A ? 1 : last]);
+            for (int e = 0; e < A; e += 3) {
+                Z.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 2 < A ? e + 2 : last]);
+                X.template consume<G, TOK>(s_jt[e], s_q[e], acc);
+                X.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 3 < A ? e + 3 : last]);
+                if (e + 1 < A) Y.template consume<G, TOK>(s_jt[e + 1], s_q[e + 1], acc);
+                Y.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 4 < A ? e + 4 : last]);
+                if (e + 2 < A) Z.template consume<G, TOK>(s_jt[e + 2], s_q[e + 2], acc);
+            }
+        } else {
+            for (int e = 0; e < A; e += 2) {
+                Y.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 1 < A ? e + 1 : last]);
+                X.template consume<G, TOK>(s_jt[e], s_q[e], acc);
+                X.issue(pplanes, pscales, nb, loff, soff, s_jt[e + 2 < A ? e + 2 : last]);
+                if (e + 1 < A) Y.template consume<G, TOK>(s_jt[e + 1], s_q[e + 1], acc);
+            }
         }
     }
 
@@ -206,7 +223,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < TOK; ++i)
-                mx = (live && tok0 + i < a.n) ? fmaxf(mx, acc[i][h]) : mx;
+                mx = (live && tok0 + i < a.n) ? fmaxf(mx, acc[h][i]) : mx;
             a.out[((size_t)p * G + h) * row + lb * kParts + part] = mx;
         }
     } else if (!FILTER) {
@@ -219,10 +236,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
 #pragma unroll
             for (int i = 0; i < TOK; i += 4) {
                 float4 v;
-                v.x = (live && tok0 + i + 0 < a.n) ? acc[i + 0][h] : -INFINITY;
-                v.y = (live && tok0 + i + 1 < a.n) ? acc[i + 1][h] : -INFINITY;
-                v.z = (live && tok0 + i + 2 < a.n) ? acc[i + 2][h] : -INFINITY;
-                v.w = (live && tok0 + i + 3 < a.n) ? acc[i + 3][h] : -INFINITY;
+                v.x = (live && tok0 + i + 0 < a.n) ? acc[h][i + 0] : -INFINITY;
+                v.y = (live && tok0 + i + 1 < a.n) ? acc[h][i + 1] : -INFINITY;
+                v.z = (live && tok0 + i + 2 < a.n) ? acc[h][i + 2] : -INFINITY;
+                v.w = (live && tok0 + i + 3 < a.n) ? acc[h][i + 3] : -INFINITY;
                 *reinterpret_cast<float4*>(o + i) = v;
             }
         }
@@ -232,11 +249,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
         const uint32_t vmask = !live || nvalid <= 0 ? 0u
                                : (nvalid >= TOK ? (TOK == 32 ? 0xFFFFFFFFu : 0xFFFFu)
                                                 : ((1u << nvalid) - 1u));
-        float* stage = s_stage[wave][lane];
+        // survivors of every head: keep[h] bit i <=> token i's score >= threshold
+        uint32_t keep[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const size_t m = (size_t)p * G + h;
-            const uint32_t tk = a.tau[m];
+            const uint32_t tk = a.tau[(size_t)p * G + h];
             // threshold as a float; +0 becomes -0 so that s - th keeps -0 scores
             float th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
             if (th == 0.0f) th = -0.0f;
@@ -244,31 +261,41 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
             uint32_t fail = 0;
 #pragma unroll
             for (int i = TOK - 1; i >= 0; --i)
-                fail = __builtin_amdgcn_alignbit(fail, __float_as_uint(acc[i][h] - th), 31);
-            uint32_t keep = ~fail & vmask;
-            const int cnt = __popc(keep);
-            int x = cnt;  // wavefront inclusive scan of cnt
+                fail = __builtin_amdgcn_alignbit(fail, __float_as_uint(acc[h][i] - th), 31);
+            keep[h] = ~fail & vmask;
+        }
+        // slots: each lane's offset within the wavefront from one LDS
+        // fetch-and-add per head, then one global fetch-and-add per head and
+        // wavefront, all issued before any result is waited for
+        uint32_t* wc = s_wcount[wave];
+        if (lane < G) wc[lane] = 0u;
+        uint32_t off[G];
 #pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int y = __shfl_up(x, o, kWave);
-                if (lane >= o) x += y;
-            }
-            const int total = __shfl(x, kWave - 1, kWave);
-            if (total == 0) continue;
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&a.counts[m], (uint32_t)total);
-            base = __shfl(base, 0, kWave);
-            if (keep) {
+        for (int h = 0; h < G; ++h) {
+            const uint32_t cnt = __popc(keep[h]);
+            off[h] = cnt ? atomicAdd(&wc[h], cnt) : 0u;
+        }
+        uint32_t base = 0;
+        if (lane < G) {
+            const uint32_t tot = wc[lane];
+            if (tot) base = atomicAdd(&a.counts[(size_t)p * G + lane], tot);
+        }
+        float* stage = s_stage[wave][lane];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            uint32_t k = keep[h];
+            const int64_t b0 = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)base, h) + off[h];
+            if (k) {
 #pragma unroll
                 for (int i = 0; i < TOK; i += 4)
                     *reinterpret_cast<float4*>(stage + i) =
-                        make_float4(acc[i][h], acc[i + 1][h], acc[i + 2][h], acc[i + 3][h]);
+                        make_float4(acc[h][i], acc[h][i + 1], acc[h][i + 2], acc[h][i + 3]);
             }
-            int64_t slot = (int64_t)base + (x - cnt);
-            uint64_t* dst = a.cand + m * a.cap;
-            while (keep) {
-                const int i = __ffs(keep) - 1;
-                keep &= keep - 1;
+            int64_t slot = b0;
+            uint64_t* dst = a.cand + ((size_t)p * G + h) * a.cap;
+            while (k) {
+                const int i = __ffs(k) - 1;
+                k &= k - 1;
                 if (slot < a.cap) dst[slot] = composite(score_key(stage[i]), (uint32_t)(tok0 + i));
                 ++slot;
             }
