@@ -142,7 +142,7 @@ struct TopkLayout {
     int64_t sample_nlb;  // logical sample blocks per pair (whole runs)
     int64_t cap;         // candidate capacity per selection
     bool lanemax;        // fused threshold from per-lane maxima of the sample
-    size_t off_tau, off_count, off_cand, bytes;        // top-k from given scores
+    size_t off_tau, off_count, off_cand, off_sorted, bytes;  // top-k from given scores
     size_t off_flags, off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };
 TopkLayout topk_layout(int P, int G, int64_t n, int k);

@@ -44,10 +44,14 @@ struct Words<16> {
     using T = uint16_t;
 };
 
-// Codes of the lane's TOK tokens for one channel, MSB-aligned: plane s sits
-// at bit 3 - s of its token's byte whatever the depth, so a t-plane prefix
-// reads as c4 = c_t * 2^(4-t) and absent planes stay zero.  Group g holds
-// tokens g, g+8, g+16, g+24 (one per byte; two bytes when TOK = 16).
+// Codes of the lane's TOK tokens for one channel.  Group g holds tokens g,
+// g+8, g+16, g+24 (one per byte; two bytes when TOK = 16), and its code sits
+// with the sign plane on bit m_g of the byte -- m_g = g for g >= 3, g + 4
+// below -- and plane s on bit m_g - s.  Then plane s reaches every group
+// with g >= 3 through one right shift by s and the others through one left
+// shift by 4 - s, so a plane costs two shifts and one AND-OR per group; the
+// byte of group g reads as c4 * 2^e_g (c4 = c_t * 2^(4-t), e_g = m_g - 3),
+// and absent planes stay zero.
 template <int TOK>
 __device__ __forceinline__ void codes(const uint32_t (&w)[4], int t, uint32_t (&c)[8])
 {
@@ -57,20 +61,22 @@ __device__ __forceinline__ void codes(const uint32_t (&w)[4], int t, uint32_t (&
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         if (s < t) {  // wavefront-uniform
-            const int pos = 3 - s;
+            const uint32_t r = w[s] >> s, l = w[s] << (4 - s);
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                const uint32_t x = (g >= pos) ? (w[s] >> (g - pos)) : (w[s] << (pos - g));
-                c[g] |= x & (lanes << pos);
-            }
+            for (int g = 0; g < 8; ++g)
+                c[g] |= (g >= 3 ? r : l) & (lanes << ((g >= 3 ? g : g + 4) - s));
         }
     }
 }
 
-// acc += q_h * khat for the lane's tokens, with khat = c4 * delta + c0 the
-// exact dequantised prefix (delta = scale/8, c0 = (1 - 2^t) * 2^-t * scale).
+// power-of-two weight of group g's byte (see codes())
+__host__ __device__ constexpr int group_exp(int g) { return g >= 3 ? g - 3 : g + 1; }
+
+// acc += q_h * khat for the lane's tokens, with khat = byte * delta_e + c0 the
+// exact dequantised prefix (delta_e = scale / 8 / 2^e for a byte weighted
+// 2^e, c0 = (1 - 2^t) * 2^-t * scale).
 template <int G, int TOK>
-__device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, float c0,
+__device__ __forceinline__ void accumulate(const uint32_t (&c)[8], const float (&delta)[5], float c0,
                                            const float (&qv)[G], float (&acc)[G][TOK])
 {
 #pragma unroll
@@ -78,7 +84,7 @@ __device__ __forceinline__ void accumulate(const uint32_t (&c)[8], float delta, 
 #pragma unroll
         for (int b = 0; b < TOK / 8; ++b) {
             const float cf = (float)((c[g] >> (8 * b)) & 0xFFu);
-            const float kh = __builtin_fmaf(cf, delta, c0);  // exact
+            const float kh = __builtin_fmaf(cf, delta[group_exp(g)], c0);  // exact
 #pragma unroll
             for (int h = 0; h < G; ++h) acc[h][g + 8 * b] = __builtin_fmaf(qv[h], kh, acc[h][g + 8 * b]);
         }
@@ -128,7 +134,9 @@ struct ChanWords {
         for (int h = 0; h < G; ++h) qv[h] = q[h];
         const uint32_t w[4] = {w0, w1, w2, w3};  // planes >= t are not read by codes()
         const float scf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc);  // v_cvt_f32_f16, exact
-        const float delta = scf * 0.125f;
+        float delta[5];  // scale / 8 / 2^e, all exact
+#pragma unroll
+        for (int e = 0; e < 5; ++e) delta[e] = scf * (0.125f / (float)(1 << e));
         const float c0 = scf * __uint_as_float((uint32_t)(127 - t) << 23) * (float)(1 - (1 << t));
         uint32_t c[8];
         codes<TOK>(w, t, c);

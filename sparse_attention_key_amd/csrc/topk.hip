@@ -16,10 +16,13 @@
 //  2. filter:    one pass over all scores appends key >= threshold to a
 //                candidate list (wavefront-aggregated atomics).
 //  3. select:    exact k largest composites of the candidates (radix select
-//                with 11-bit digits in LDS, then an LDS bitonic sort).  A
-//                selection whose candidates overflowed their capacity runs
-//                the same select directly over all its scores instead.
-//  4. union:     LDS sort of the G*k indices of a pair, duplicates dropped.
+//                with 11-bit digits, the last levels in LDS), each winner
+//                placed by its rank; a second rank by token index gives the
+//                winners sorted by index.  A selection whose candidates
+//                overflowed their capacity runs the same select directly over
+//                all its scores instead.
+//  4. union:     merge of the G index-sorted lists of a pair, duplicates
+//                dropped.
 #include "common.h"
 
 namespace fathom {
@@ -79,13 +82,6 @@ __device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh)
     for (int w = 0; w < wave; ++w) off += sh.wsum[w];
     __syncthreads();
     return off + x - v;
-}
-
-__device__ __forceinline__ int pow2_ceil(int x)
-{
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
 }
 
 // One radix level: histogram of the 11-bit digit at `sft` over the elements
@@ -262,7 +258,7 @@ __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ s
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int64_t n, int64_t npad, const uint32_t* __restrict__ counts,
     const uint64_t* __restrict__ cand, int64_t cap, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_val)
+    float* __restrict__ topk_val, int32_t* __restrict__ sorted_idx)
 {
     __shared__ SelShared sh;
     const int64_t m = blockIdx.x;
@@ -286,50 +282,80 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
     __syncthreads();
+    // rank of each winner by composite (its output position) and by token
+    // index (its position in the index-sorted list the union merges);
+    // index i < index j exactly when ~i > ~j in the low word
     for (int i = threadIdx.x; i < k; i += blockDim.x) {
         const uint64_t v = sh.buf[i];
-        int r = 0;
-        for (int j = 0; j < k; ++j) r += sh.buf[j] > v ? 1 : 0;
-        topk_idx[m * k + r] = (int32_t)(~(uint32_t)v);
+        const uint32_t lo = (uint32_t)v;
+        int r = 0, ri = 0;
+        for (int j = 0; j < k; ++j) {
+            const uint64_t u = sh.buf[j];
+            r += u > v ? 1 : 0;
+            ri += (uint32_t)u > lo ? 1 : 0;
+        }
+        topk_idx[m * k + r] = (int32_t)(~lo);
         if (topk_val) topk_val[m * k + r] = key_score((uint32_t)(v >> 32));
+        sorted_idx[m * k + ri] = (int32_t)(~lo);
     }
 }
 
-__global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __restrict__ topk_idx,
+// Union of the G winner lists of a pair, each sorted by token index: every
+// element's place in the merged order is its own position plus the number
+// of elements of each other list that precede it (binary search; equal
+// indices ordered by list), then adjacent duplicates are dropped.
+__global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __restrict__ sorted_idx,
                                                             int G, int k,
                                                             int32_t* __restrict__ union_idx,
                                                             int32_t* __restrict__ union_len)
 {
+    constexpr int kPer = kMaxUnion / kSelThreads;
     __shared__ int32_t a[kMaxUnion];
     __shared__ uint32_t wsum[kSelThreads / kWave];
     const int p = blockIdx.x;
     const int total = G * k;
-    const int len = pow2_ceil(total);
-    for (int i = threadIdx.x; i < len; i += blockDim.x)
-        a[i] = i < total ? topk_idx[(size_t)p * total + i] : 0x7FFFFFFF;
+    const int32_t* src = sorted_idx + (size_t)p * total;
+    for (int i = threadIdx.x; i < total; i += blockDim.x) a[i] = src[i];
     __syncthreads();
-    for (int k2 = 2; k2 <= len; k2 <<= 1)
-        for (int j = k2 >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < len; i += blockDim.x) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const int32_t x = a[i], y = a[ixj];
-                    const bool asc = (i & k2) == 0;
-                    if (asc ? (x > y) : (x < y)) {
-                        a[i] = y;
-                        a[ixj] = x;
-                    }
+    int32_t val[kPer];
+    int pos[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = threadIdx.x + u * (int)blockDim.x;
+        pos[u] = -1;
+        val[u] = 0;
+        if (e < total) {
+            const int h = e / k;
+            const int32_t x = a[e];
+            int r = e - h * k;
+            for (int h2 = 0; h2 < G; ++h2) {
+                if (h2 == h) continue;
+                const int32_t* l = a + h2 * k;
+                int lo = 0, hi = k;  // first element of list h2 placed after x
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    const bool before = h2 < h ? l[mid] <= x : l[mid] < x;
+                    if (before) lo = mid + 1;
+                    else hi = mid;
                 }
+                r += lo;
             }
-            __syncthreads();
+            val[u] = x;
+            pos[u] = r;
         }
-    // each thread owns a contiguous run of per = len / blockDim (>= 1) slots
-    const int per = (len + blockDim.x - 1) / blockDim.x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if (pos[u] >= 0) a[pos[u]] = val[u];
+    __syncthreads();
+    // each thread owns a contiguous run of the merged order; first
+    // occurrences are counted, scanned and written out
+    const int per = (total + blockDim.x - 1) / blockDim.x;
     const int beg = threadIdx.x * per;
     uint32_t cnt = 0;
-    for (int i = beg; i < beg + per && i < len; ++i)
-        cnt += (a[i] != 0x7FFFFFFF && (i == 0 || a[i] != a[i - 1])) ? 1u : 0u;
-    // exclusive scan of cnt
+    for (int i = beg; i < beg + per && i < total; ++i)
+        cnt += (i == 0 || a[i] != a[i - 1]) ? 1u : 0u;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     uint32_t x = cnt;
     for (int o = 1; o < kWave; o <<= 1) {
@@ -343,10 +369,10 @@ __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __res
         if (w < wave) off += wsum[w];
         all += wsum[w];
     }
-    uint32_t pos = off + x - cnt;
+    uint32_t q = off + x - cnt;
     int32_t* out = union_idx + (size_t)p * total;
-    for (int i = beg; i < beg + per && i < len; ++i)
-        if (a[i] != 0x7FFFFFFF && (i == 0 || a[i] != a[i - 1])) out[pos++] = a[i];
+    for (int i = beg; i < beg + per && i < total; ++i)
+        if (i == 0 || a[i] != a[i - 1]) out[q++] = a[i];
     for (int i = (int)all + threadIdx.x; i < total; i += blockDim.x) out[i] = -1;
     if (threadIdx.x == 0) union_len[p] = (int32_t)all;
 }
@@ -373,7 +399,8 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k)
     L.off_tau = 0;
     L.off_count = up((size_t)L.m * 4);
     L.off_cand = up(L.off_count + (size_t)L.m * 4);
-    L.bytes = L.off_cand + (size_t)L.m * (size_t)L.cap * 8;
+    L.off_sorted = up(L.off_cand + (size_t)L.m * (size_t)L.cap * 8);
+    L.bytes = L.off_sorted + (size_t)L.m * (size_t)k * 4;
     L.off_flags = up(L.bytes);
     L.off_sample = up(L.off_flags + (size_t)P * 4);
     L.off_repair = up(L.off_sample + (size_t)L.m * (size_t)L.sample_nlb * 64 * 4);
@@ -409,9 +436,10 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
         filter_kernel<<<dim3((unsigned)L.m, (unsigned)gy), 256, 0, st>>>(scores, n, npad, tau,
                                                                            counts, cand, L.cap);
     }
+    int32_t* sorted = (int32_t*)(w + L.off_sorted);
     select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
-                                                              k, topk_idx, topk_val);
-    union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(topk_idx, G, k, union_idx, union_len);
+                                                              k, topk_idx, topk_val, sorted);
+    union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(sorted, G, k, union_idx, union_len);
     return hipGetLastError();
 }
 
@@ -466,9 +494,10 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         a.only = flags;
         if ((e = launch_scan_args(a, P, G, 0, st)) != hipSuccess) return e;
         // exact top-k of the candidates (or of the repaired scores), union
+        int32_t* sorted = (int32_t*)(w + L.off_sorted);
         select_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(repair, n, npad, counts, cand,
-                                                                  L.cap, k, topk_idx, topk_val);
-        union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(topk_idx, G, k, union_idx, union_len);
+                                                                  L.cap, k, topk_idx, topk_val, sorted);
+        union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(sorted, G, k, union_idx, union_len);
     }
     return hipGetLastError();
 }
