@@ -29,7 +29,6 @@ HBM_PEAK_GBS = 8000.0
 # fp32 vector peak: 256 CUs x 64 lanes x 2.4 GHz x 2 FLOP per FMA x 2 (packed
 # dual FMA).  Without packed fp32 a lane retires one FMA per cycle: half that.
 FP32_VECTOR_PEAK_TFLOPS = 157.3
-VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9
 
 
 def log(*a):
@@ -391,13 +390,15 @@ def main():
                 "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
                 "traffic": prof.get("hbm_bytes_per_launch"), "alg_flops_per_launch": alg_flops,
                 "peak_without_packed_fp32": FP32_VECTOR_PEAK_TFLOPS / 2,
-                "valu_busy": prof.get("valu_busy"), "valu_lane_ops_per_elem": ops,
+                # VALU issue measured by rocprofv3 on this kernel source: share
+                # of SIMD quad-cycles issuing a VALU instruction, instructions
+                # per quad-cycle (two can issue together), instructions per
+                # (token, active channel)
+                "valu_busy": prof.get("valu_busy"), "valu_instr_per_elem": ops,
+                "valu_instr_per_quad_cycle": (prof.get("valu") or {}).get("valu_instr_per_simd_quad_cycle"),
                 "hbm": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes,
-                        "measured_read_probe_GBs": link["hbm_read_probe"],
-                        # the rate the VALU allows at the measured instruction count
-                        "valu_ceiling_GBs": (round(VALU_LANE_OPS_PER_S / ops * alg_bytes / elems / 1e9, 1)
-                                             if ops else None)}}
+                        "measured_read_probe_GBs": link["hbm_read_probe"]}}
     else:
         peak = link["zero_copy_read"]
         roof = {"bound": "host_link", "kernel": "scan_kernel (filter)", "achieved": round(achieved, 2),
