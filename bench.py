@@ -237,6 +237,28 @@ def fetch_probe(F, w, out, device):
             "source": "mapped pinned host memory, K|V rows of 512 B (bf16, D=128)"}
 
 
+def append_probe(F, w, planes, scales, device):
+    """Cost of ingesting one new key per pair: the block of the last token is
+    repacked from its raw keys (its scale is recomputed from all of them), for
+    every pair in one call.  The bench index is dense, so the last block is
+    repacked in place; it runs after every timed step."""
+    import torch
+
+    tok0 = (w.nb - 1) * 64
+    m = w.n - tok0
+    keys = (torch.randn((w.P, m, w.D), device=device) * 2).to(torch.bfloat16)
+    F.pack_range(keys, tok0, planes, scales)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        F.pack_range(keys, tok0, planes, scales)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"pairs": w.P, "tokens_in_block": m, "us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2)}
+
+
 def cpu_baseline(w, q, s2, budget, mode, pairs, threads, rot=None):
     """Time the CPU oracle (as it stands) on a bounded sample of pairs: the
     same plan + scores + top-k + union per pair, run `threads` pairs at a
@@ -428,6 +450,9 @@ def main():
     if w.n >= (1 << 17):
         res["fetch"] = fetch_probe(F, w, out, dev)
         log(f"winner-row fetch: {res['fetch']}")
+    if host is None:
+        res["append"] = append_probe(F, w, planes, scales, dev)
+        log(f"append (repack the last block of every pair): {res['append']}")
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q_np, s2_np, budget, a.mode, a.cpu_pairs, a.cpu_threads,
                                            rot=rot_np)

@@ -28,12 +28,15 @@
  *    head) 1 <= G <= 8; n (tokens) >= 1.  nb = ceil(n / 64) blocks,
  *    npad = 64 * nb.  Tokens n..npad-1 of the last block are padding.
  *
- * Index layout (per pair):
- *    planes [D][4][nb] uint64 -- word (j, s, b): bit i is bit (3 - s) of the
- *                                4-bit code of token 64*b + i in channel j
- *                                (s = 0 is the sign plane).  A channel's
- *                                t-plane prefix is t*nb contiguous words.
- *    scales [D][nb]    uint16 -- IEEE binary16 block max |x| of (channel, block).
+ * Index layout (per pair), with rows of L blocks:
+ *    planes [D][4][L] uint64 -- word (j, s, b): bit i is bit (3 - s) of the
+ *                               4-bit code of token 64*b + i in channel j
+ *                               (s = 0 is the sign plane).  A channel's
+ *                               t-plane prefix is t*L contiguous words.
+ *    scales [D][L]    uint16 -- IEEE binary16 block max |x| of (channel, block).
+ *  L = nb for a dense index.  An index meant to grow is allocated with a
+ *  capacity of nb_cap >= nb blocks per row (L = nb_cap) and filled or
+ *  extended with fathom_pack_range; calls that read it take nb_cap.
  *  Footprint: 68 bytes per token per pair at D = 128.
  */
 #ifndef FATHOM_H
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 1
+#define FATHOM_ABI_VERSION 2
 
 #define FATHOM_OK 0
 #define FATHOM_ERR_ARG (-1)         /* null pointer, bad enum, bad budget/k  */
@@ -89,6 +92,30 @@ int fathom_pack(const void* keys, int32_t dtype, int32_t P, int64_t n, int32_t D
                 const float* rot, uint64_t* planes, uint16_t* scales, void* stream);
 
 /*
+ * fathom_pack_range -- pack tokens [tok0, tok0 + m) of every pair into an
+ * index with rows of nb_cap blocks, leaving all other blocks untouched.
+ * Each block is quantised on its own (its scale is its own block max), so
+ * packing a range gives bit for bit the words and scales that fathom_pack
+ * of the whole sequence gives for those blocks.  Appending to a decode
+ * cache: when token n-1 arrives, pack the raw keys of its block (tokens
+ * 64*floor((n-1)/64) .. n-1, held by the caller's KV cache) with
+ * tok0 = 64*floor((n-1)/64); the block's scale is recomputed from all of
+ * them.  The pages do not describe appends; this is the plainest reading of
+ * their per-block quantiser.
+ *
+ *   keys   [P][m][D]  the keys of the range, as in fathom_pack
+ *   tok0   first token, a multiple of 64
+ *   m      tokens in the range, 1 <= m, tok0 + m <= 64 * nb_cap
+ *   rot, planes, scales  as in fathom_pack, rows of nb_cap blocks
+ * Tokens of the last block beyond the range are padding (code 8).
+ * Errors: ERR_ARG (null, dtype, tok0 not a multiple of 64), ERR_SHAPE,
+ * ERR_ALIGN.
+ */
+int fathom_pack_range(const void* keys, int32_t dtype, int32_t P, int64_t tok0, int64_t m,
+                      int32_t D, const float* rot, uint64_t* planes, uint16_t* scales,
+                      int64_t nb_cap, void* stream);
+
+/*
  * fathom_plan -- per-pair read plan (method section two; basis section).
  *
  *   q       [P][G][D] float32 query heads of each KV-head group
@@ -123,6 +150,8 @@ int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P
  * shift-and-mask per extracted bit and G multiply-adds per element).
  *
  *   planes, scales       the index (may be host-mapped memory)
+ *   nb_cap               blocks per index row: 0 for a dense index (nb),
+ *                        else the capacity it was allocated with (>= nb)
  *   depth, active, n_active, q_used   a plan from fathom_plan
  *   scores [P][G][npad]  float32 output.  Score of token i for head h:
  *       s = 0; for each active channel j in ascending order:
@@ -133,8 +162,9 @@ int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P
  * Errors: ERR_ARG (null), ERR_SHAPE, ERR_ALIGN.
  */
 int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
-                const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                const float* q_used, int32_t G, float* scores, void* stream);
+                int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                const int32_t* n_active, const float* q_used, int32_t G, float* scores,
+                void* stream);
 
 /*
  * fathom_topk -- the k best keys of every query head and their union per KV
@@ -177,10 +207,10 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
  */
 size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k);
 int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
-                     const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                     const float* q_used, int32_t G, int32_t k, int32_t* topk_idx, float* topk_val,
-                     int32_t* union_idx, int32_t* union_len, void* ws, size_t ws_bytes,
-                     void* stream);
+                     int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                     const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                     int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * fathom_scan_topk_stage -- the three stages of fathom_scan_topk as separate
@@ -195,10 +225,11 @@ int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int32_t P, 
  * Errors: ERR_ARG for a stage outside 1..3, else as fathom_scan_topk.
  */
 int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t* scales, int32_t P,
-                           int32_t D, int64_t n, const uint8_t* depth, const int16_t* active,
-                           const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
-                           int32_t* topk_idx, float* topk_val, int32_t* union_idx,
-                           int32_t* union_len, void* ws, size_t ws_bytes, void* stream);
+                           int32_t D, int64_t n, int64_t nb_cap, const uint8_t* depth,
+                           const int16_t* active, const int32_t* n_active, const float* q_used,
+                           int32_t G, int32_t k, int32_t* topk_idx, float* topk_val,
+                           int32_t* union_idx, int32_t* union_len, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * fathom_gather_rows -- the winner-row fetch that follows the selection:

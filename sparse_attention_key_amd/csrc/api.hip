@@ -11,11 +11,24 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? FATHOM_OK : FATHOM_ERR_HIP; }
 
+constexpr int64_t kMaxTokens = ((int64_t)1 << 31) - 64;  // token index fits int32
+constexpr int64_t kMaxRowBlocks = (int64_t)1 << 25;      // 64 * this = 2^31 tokens
+
 inline int check_shape(int32_t P, int64_t n, int32_t D)
 {
     if (P < 1 || P > kMaxPairs || n < 1 || D < 1 || D > kMaxD) return FATHOM_ERR_SHAPE;
-    if (n > ((int64_t)1 << 31) - 64) return FATHOM_ERR_SHAPE;  // token index fits int32
+    if (n > kMaxTokens) return FATHOM_ERR_SHAPE;
     return FATHOM_OK;
+}
+
+// Row stride of the index in blocks: 0 selects ceil(n / 64); anything else
+// must hold the n tokens.  Returns -1 when invalid.
+inline int64_t row_blocks(int64_t n, int64_t nb_cap)
+{
+    const int64_t nb = (n + 63) / 64;
+    if (nb_cap == 0) return nb;
+    if (nb_cap < nb || nb_cap > kMaxRowBlocks) return -1;
+    return nb_cap;
 }
 
 }  // namespace
@@ -47,7 +60,24 @@ int fathom_pack(const void* keys, int32_t dtype, int32_t P, int64_t n, int32_t D
     if (s) return s;
     if (!aligned16(keys) || !aligned16(planes) || !aligned16(scales) || (rot && !aligned16(rot)))
         return FATHOM_ERR_ALIGN;
-    return hip_status(launch_pack(keys, dtype, P, n, D, rot, planes, scales, (hipStream_t)stream));
+    return hip_status(
+        launch_pack(keys, dtype, P, 0, n, D, rot, planes, scales, (n + 63) / 64, (hipStream_t)stream));
+}
+
+int fathom_pack_range(const void* keys, int32_t dtype, int32_t P, int64_t tok0, int64_t m,
+                      int32_t D, const float* rot, uint64_t* planes, uint16_t* scales,
+                      int64_t nb_cap, void* stream)
+{
+    if (!keys || !planes || !scales) return FATHOM_ERR_ARG;
+    if (dtype != FATHOM_DTYPE_F32 && dtype != FATHOM_DTYPE_BF16) return FATHOM_ERR_ARG;
+    int s = check_shape(P, m, D);
+    if (s) return s;
+    if (tok0 < 0 || tok0 % 64 != 0) return FATHOM_ERR_ARG;
+    if (nb_cap < 1 || nb_cap > kMaxRowBlocks || tok0 + m > 64 * nb_cap) return FATHOM_ERR_SHAPE;
+    if (!aligned16(keys) || !aligned16(planes) || !aligned16(scales) || (rot && !aligned16(rot)))
+        return FATHOM_ERR_ALIGN;
+    return hip_status(
+        launch_pack(keys, dtype, P, tok0, m, D, rot, planes, scales, nb_cap, (hipStream_t)stream));
 }
 
 int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P, int32_t G,
@@ -74,18 +104,21 @@ int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P
 }
 
 int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
-                const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                const float* q_used, int32_t G, float* scores, void* stream)
+                int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                const int32_t* n_active, const float* q_used, int32_t G, float* scores,
+                void* stream)
 {
     if (!planes || !scales || !depth || !active || !n_active || !q_used || !scores)
         return FATHOM_ERR_ARG;
     int s = check_shape(P, n, D);
     if (s) return s;
+    const int64_t ldb = row_blocks(n, nb_cap);
+    if (ldb < 0) return FATHOM_ERR_SHAPE;
     if (G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
     const void* ps[] = {planes, scales, depth, active, n_active, q_used, scores};
     for (const void* p : ps)
         if (!aligned16(p)) return FATHOM_ERR_ALIGN;
-    return hip_status(launch_scan(planes, scales, P, D, n, depth, active, n_active, q_used, G,
+    return hip_status(launch_scan(planes, scales, P, D, n, ldb, depth, active, n_active, q_used, G,
                                   scores, (hipStream_t)stream));
 }
 
@@ -122,7 +155,7 @@ size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t
 }
 
 static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
-                          int64_t n, const uint8_t* depth, const int16_t* active,
+                          int64_t n, int64_t nb_cap, const uint8_t* depth, const int16_t* active,
                           const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
                           int32_t* topk_idx, float* topk_val, int32_t* union_idx,
                           int32_t* union_len, void* ws, size_t ws_bytes, void* stream, int stages)
@@ -131,6 +164,8 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
     if ((stages & 4) && (!topk_idx || !union_idx || !union_len)) return FATHOM_ERR_ARG;
     int s = check_shape(P, n, D);
     if (s) return s;
+    const int64_t ldb = row_blocks(n, nb_cap);
+    if (ldb < 0) return FATHOM_ERR_SHAPE;
     if (G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
     if (k < 1 || k > n) return FATHOM_ERR_ARG;
     if (k > kMaxK || G * k > kMaxUnion) return FATHOM_ERR_UNSUPPORTED;
@@ -152,6 +187,7 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
     a.D = D;
     a.n = n;
     a.nb = (n + 63) / 64;
+    a.ldb = ldb;
     a.depth = depth;
     a.active = active;
     a.n_active = n_active;
@@ -161,23 +197,26 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
 }
 
 int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
-                     const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                     const float* q_used, int32_t G, int32_t k, int32_t* topk_idx, float* topk_val,
-                     int32_t* union_idx, int32_t* union_len, void* ws, size_t ws_bytes, void* stream)
+                     int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                     const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                     int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                     void* ws, size_t ws_bytes, void* stream)
 {
-    return scan_topk_impl(planes, scales, P, D, n, depth, active, n_active, q_used, G, k, topk_idx,
-                          topk_val, union_idx, union_len, ws, ws_bytes, stream, 7);
+    return scan_topk_impl(planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, k,
+                          topk_idx, topk_val, union_idx, union_len, ws, ws_bytes, stream, 7);
 }
 
 int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t* scales, int32_t P,
-                           int32_t D, int64_t n, const uint8_t* depth, const int16_t* active,
-                           const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
-                           int32_t* topk_idx, float* topk_val, int32_t* union_idx,
-                           int32_t* union_len, void* ws, size_t ws_bytes, void* stream)
+                           int32_t D, int64_t n, int64_t nb_cap, const uint8_t* depth,
+                           const int16_t* active, const int32_t* n_active, const float* q_used,
+                           int32_t G, int32_t k, int32_t* topk_idx, float* topk_val,
+                           int32_t* union_idx, int32_t* union_len, void* ws, size_t ws_bytes,
+                           void* stream)
 {
     if (stage < 1 || stage > 3) return FATHOM_ERR_ARG;
-    return scan_topk_impl(planes, scales, P, D, n, depth, active, n_active, q_used, G, k, topk_idx,
-                          topk_val, union_idx, union_len, ws, ws_bytes, stream, 1 << (stage - 1));
+    return scan_topk_impl(planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, k,
+                          topk_idx, topk_val, union_idx, union_len, ws, ws_bytes, stream,
+                          1 << (stage - 1));
 }
 
 int fathom_gather_rows(const void* table, int64_t table_rows, int64_t row_bytes,

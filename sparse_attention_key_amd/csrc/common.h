@@ -100,21 +100,26 @@ __device__ __forceinline__ float wave_max_f32(float v)
 
 // --------------------------------------------------------- host launchers
 
-hipError_t launch_pack(const void* keys, int dtype, int P, int64_t n, int D, const float* rot,
-                       uint64_t* planes, uint16_t* scales, hipStream_t st);
+// Packs tokens [tok0, tok0 + m) of every pair (tok0 a multiple of 64) into an
+// index whose channel rows hold ldb blocks.
+hipError_t launch_pack(const void* keys, int dtype, int P, int64_t tok0, int64_t m, int D,
+                       const float* rot, uint64_t* planes, uint16_t* scales, int64_t ldb,
+                       hipStream_t st);
 hipError_t launch_plan(const float* q, const float* sigma2, const float* rot, int P, int G, int D,
                        int budget, int mode, uint8_t* depth, int16_t* active, int32_t* n_active,
                        float* theta, float* q_used, hipStream_t st);
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,
-                       const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                       const float* q_used, int G, float* scores, hipStream_t st);
+                       int64_t ldb, const uint8_t* depth, const int16_t* active,
+                       const int32_t* n_active, const float* q_used, int G, float* scores,
+                       hipStream_t st);
 
 // Arguments of the scan kernels (see scan.hip).
 struct ScanArgs {
     const uint64_t* planes;
     const uint16_t* scales;
     int D;
-    int64_t n, nb;
+    int64_t n, nb;         // tokens, and the blocks that hold them
+    int64_t ldb;           // blocks per channel row of the index (>= nb)
     const uint8_t* depth;
     const int16_t* active;
     const int32_t* n_active;

@@ -3,17 +3,21 @@
 // code, one fp16 scale per 64-token block, bit p of the block's 64 codes in
 // one 64-bit plane word, planes laid out along the sequence per channel).
 //
-// One workgroup (4 wavefronts) packs 16 consecutive blocks of one pair.  A
-// wavefront owns one block at a time with lane i = token i, so the block max
-// is a wavefront max-reduction and each plane word is one ballot.  Words are
-// collected in LDS as [channel][plane][16 blocks] and written out as whole
-// 128-byte rows, so the scattered per-block words never hit HBM one by one.
+// One workgroup (4 wavefronts) packs up to 8 consecutive blocks of one pair,
+// one block at a time: the block's 64 keys are read with coalesced 16-byte
+// loads into LDS, then the wavefronts share out the channels -- lane i =
+// token i, so the block max of a channel is a wavefront max-reduction and
+// each plane word is one ballot.  Words are collected in LDS as
+// [channel][plane][blocks] and written out as whole row segments, so the
+// scattered per-block words never hit HBM one by one.  A one-block call (an
+// append) thus uses all four wavefronts.
 #include "common.h"
 
 namespace fathom {
 namespace {
 
-constexpr int kRun = 16;  // blocks per workgroup
+constexpr int kRun = 8;  // blocks per workgroup
+constexpr int kKeyStride = kMaxD + 1;  // LDS row of one token's keys (padded)
 
 // Exact floor(x / delta) + 8, clamped to the 4-bit range.  delta = scale/8
 // has at most 11 significant bits and |x / delta| stays below ~9 inside a
@@ -29,47 +33,96 @@ __device__ __forceinline__ uint32_t quant_code(float x, float delta, float inv)
     return (uint32_t)f;
 }
 
+// Copies the keys of tokens [t0, t0 + 64) (those below m) of pair p into
+// s_keys[token][channel] as floats, with 16-byte loads along each row.
 template <int DTYPE>
-__device__ __forceinline__ float load_key(const void* keys, size_t off)
+__device__ __forceinline__ void stage_keys(const void* keys, int64_t m, int D, int p, int64_t t0,
+                                           float* s_keys)
 {
-    if (DTYPE == 0) return ((const float*)keys)[off];
-    uint32_t b = ((const uint16_t*)keys)[off];
-    return __uint_as_float(b << 16);  // bfloat16 widens exactly
+    constexpr int per = DTYPE == 0 ? 4 : 8;  // elements per 16-byte load
+    const int vecs = D / per;                // D is a multiple of 8 for this path
+    for (int e = threadIdx.x; e < 64 * vecs; e += blockDim.x) {
+        const int i = e / vecs, c = (e - i * vecs) * per;
+        const int64_t tok = t0 + i;
+        float v[8];
+        if (tok < m) {
+            const size_t off = ((size_t)p * m + (size_t)tok) * D + c;
+            if (DTYPE == 0) {
+                const float4 f = *reinterpret_cast<const float4*>((const float*)keys + off);
+                v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+            } else {
+                const uint4 u = *reinterpret_cast<const uint4*>((const uint16_t*)keys + off);
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {  // bfloat16 widens exactly
+                    v[2 * k] = __uint_as_float(w[k] << 16);
+                    v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < per; ++k) s_keys[i * kKeyStride + c + k] = v[k];
+    }
 }
 
+// Scalar fallback for D not a multiple of 8 (one element per load).
+template <int DTYPE>
+__device__ __forceinline__ void stage_keys_scalar(const void* keys, int64_t m, int D, int p,
+                                                  int64_t t0, float* s_keys)
+{
+    for (int e = threadIdx.x; e < 64 * D; e += blockDim.x) {
+        const int i = e / D, c = e - i * D;
+        const int64_t tok = t0 + i;
+        float v = 0.0f;
+        if (tok < m) {
+            const size_t off = ((size_t)p * m + (size_t)tok) * D + c;
+            v = DTYPE == 0 ? ((const float*)keys)[off]
+                           : __uint_as_float((uint32_t)((const uint16_t*)keys)[off] << 16);
+        }
+        s_keys[i * kKeyStride + c] = v;
+    }
+}
+
+// Blocks [b0, b0 + nbk) of every pair, from the m keys [P][m][D] that start
+// at token 64 * b0; the index rows hold ldb blocks.
 template <int DTYPE, bool ROT>
-__global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ keys, int64_t n,
-                                                   int D, int64_t nb,
+__global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ keys, int64_t m,
+                                                   int D, int64_t bfirst, int64_t nbk, int64_t ldb,
                                                    const float* __restrict__ rot,
                                                    uint64_t* __restrict__ planes,
                                                    uint16_t* __restrict__ scales)
 {
-    __shared__ uint64_t s_words[kMaxD * 4 * kRun];  // 64 KB
+    __shared__ uint64_t s_words[kMaxD * 4 * kRun];  // 32 KB
     __shared__ uint16_t s_scale[kMaxD * kRun];
+    __shared__ float s_keys[64 * kKeyStride];       // 33 KB
 
     const int p = blockIdx.y;
-    const int64_t b0 = (int64_t)blockIdx.x * kRun;
+    const int64_t b0 = (int64_t)blockIdx.x * kRun;  // relative to bfirst
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const float* U = ROT ? rot + (size_t)p * D * D : nullptr;
+    const int runs = (int)((nbk - b0) < kRun ? (nbk - b0) : kRun);
 
-    for (int r = wave; r < kRun; r += 4) {
-        const int64_t b = b0 + r;
-        if (b >= nb) break;
-        const int64_t tok = b * 64 + lane;
-        const bool valid = tok < n;
-        const size_t row = ((size_t)p * n + (size_t)(valid ? tok : 0)) * D;
-        for (int j = 0; j < D; ++j) {
+    for (int r = 0; r < runs; ++r) {
+        const int64_t tok = (b0 + r) * 64 + lane;  // position among the m keys
+        const bool valid = tok < m;
+        if (D % 8 == 0) stage_keys<DTYPE>(keys, m, D, p, (b0 + r) * 64, s_keys);
+        else stage_keys_scalar<DTYPE>(keys, m, D, p, (b0 + r) * 64, s_keys);
+        __syncthreads();
+        const float* kr = s_keys + lane * kKeyStride;
+        for (int j = wave; j < D; j += 4) {
             float x;
             if (ROT) {
                 float acc = 0.0f;
-                for (int d = 0; d < D; ++d)
-                    acc = __builtin_fmaf(U[(size_t)d * D + j], load_key<DTYPE>(keys, row + d), acc);
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(U[(size_t)d * D + j], kr[d], acc);
                 x = acc;
             } else {
-                x = load_key<DTYPE>(keys, row + j);
+                x = kr[j];
             }
-            const float m = wave_max_f32(valid ? fabsf(x) : 0.0f);
-            const uint32_t sb = f32_to_f16_rne_sat(m);
+            const float mx = wave_max_f32(valid ? fabsf(x) : 0.0f);
+            const uint32_t sb = f32_to_f16_rne_sat(mx);
             const float delta = f16_bits_to_f32(sb) * 0.125f;
             const float inv = 1.0f / delta;
             const uint32_t c = valid ? quant_code(x, delta, inv) : 8u;
@@ -80,33 +133,33 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ keys
             }
             if (lane == 0) s_scale[j * kRun + r] = (uint16_t)sb;
         }
+        __syncthreads();  // s_keys is refilled for the next block
     }
-    __syncthreads();
 
-    const int runs = (int)((nb - b0) < kRun ? (nb - b0) : kRun);
     for (int e = threadIdx.x; e < D * 4 * kRun; e += blockDim.x) {
         const int r = e % kRun, js = e / kRun;
-        if (r < runs) planes[((size_t)p * D * 4 + js) * nb + b0 + r] = s_words[e];
+        if (r < runs) planes[((size_t)p * D * 4 + js) * ldb + bfirst + b0 + r] = s_words[e];
     }
     for (int e = threadIdx.x; e < D * kRun; e += blockDim.x) {
         const int r = e % kRun, j = e / kRun;
-        if (r < runs) scales[((size_t)p * D + j) * nb + b0 + r] = s_scale[e];
+        if (r < runs) scales[((size_t)p * D + j) * ldb + bfirst + b0 + r] = s_scale[e];
     }
 }
 
 }  // namespace
 
-hipError_t launch_pack(const void* keys, int dtype, int P, int64_t n, int D, const float* rot,
-                       uint64_t* planes, uint16_t* scales, hipStream_t st)
+hipError_t launch_pack(const void* keys, int dtype, int P, int64_t tok0, int64_t m, int D,
+                       const float* rot, uint64_t* planes, uint16_t* scales, int64_t ldb,
+                       hipStream_t st)
 {
-    const int64_t nb = (n + 63) / 64;
-    dim3 grid((unsigned)((nb + kRun - 1) / kRun), (unsigned)P);
+    const int64_t bfirst = tok0 / 64, nbk = (m + 63) / 64;
+    dim3 grid((unsigned)((nbk + kRun - 1) / kRun), (unsigned)P);
     if (dtype == 0) {
-        if (rot) pack_kernel<0, true><<<grid, 256, 0, st>>>(keys, n, D, nb, rot, planes, scales);
-        else pack_kernel<0, false><<<grid, 256, 0, st>>>(keys, n, D, nb, rot, planes, scales);
+        if (rot) pack_kernel<0, true><<<grid, 256, 0, st>>>(keys, m, D, bfirst, nbk, ldb, rot, planes, scales);
+        else pack_kernel<0, false><<<grid, 256, 0, st>>>(keys, m, D, bfirst, nbk, ldb, rot, planes, scales);
     } else {
-        if (rot) pack_kernel<1, true><<<grid, 256, 0, st>>>(keys, n, D, nb, rot, planes, scales);
-        else pack_kernel<1, false><<<grid, 256, 0, st>>>(keys, n, D, nb, rot, planes, scales);
+        if (rot) pack_kernel<1, true><<<grid, 256, 0, st>>>(keys, m, D, bfirst, nbk, ldb, rot, planes, scales);
+        else pack_kernel<1, false><<<grid, 256, 0, st>>>(keys, m, D, bfirst, nbk, ldb, rot, planes, scales);
     }
     return hipGetLastError();
 }

@@ -102,15 +102,15 @@ struct ChanWords {
     uint32_t w0, w1, w2, w3, sc;
 
     __device__ __forceinline__ void issue(const uint64_t* pplanes, const uint16_t* pscales,
-                                          int64_t nb, uint32_t loff, uint32_t soff, int jt_lds)
+                                          int64_t ldb, uint32_t loff, uint32_t soff, int jt_lds)
     {
         const int jt = __builtin_amdgcn_readfirstlane(jt_lds);
         const int j = jt & 0xFFFF, t = jt >> 16;
-        const int row = (int)(nb * 8);
+        const int row = (int)(ldb * 8);
         __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(pplanes + (size_t)j * 4 * nb), (short)0, 4 * row, 0x00020000);
+            (void*)(pplanes + (size_t)j * 4 * ldb), (short)0, 4 * row, 0x00020000);
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(pscales + (size_t)j * nb), (short)0, (int)(nb * 2), 0x00020000);
+            (void*)(pscales + (size_t)j * ldb), (short)0, (int)(ldb * 2), 0x00020000);
         if (sizeof(WT) == 4) {
             w0 = __builtin_amdgcn_raw_buffer_load_b32(rp, loff, 0, 0);
             w1 = __builtin_amdgcn_raw_buffer_load_b32(rp, loff, t > 1 ? row : 0, 0);
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     const int64_t phys = (lb / kRun) * kRun * a.stride + (lb % kRun);
     const bool live = lb < a.nlb && phys < a.nb;
     const int64_t blk = live ? phys : 0;
-    const int64_t nb = a.nb;
+    const int64_t nb = a.ldb;  // row stride of the index, in blocks
     const uint64_t* pplanes = a.planes + (size_t)p * a.D * 4 * nb;  // uniform
     const uint16_t* pscales = a.scales + (size_t)p * a.D * nb;
     const uint32_t loff = (uint32_t)(blk * 8 + part * (int)sizeof(WT));
@@ -346,8 +346,9 @@ hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream
 }
 
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,
-                       const uint8_t* depth, const int16_t* active, const int32_t* n_active,
-                       const float* q_used, int G, float* scores, hipStream_t st)
+                       int64_t ldb, const uint8_t* depth, const int16_t* active,
+                       const int32_t* n_active, const float* q_used, int G, float* scores,
+                       hipStream_t st)
 {
     ScanArgs a{};
     a.planes = planes;
@@ -355,6 +356,7 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, in
     a.D = D;
     a.n = n;
     a.nb = (n + 63) / 64;
+    a.ldb = ldb;
     a.depth = depth;
     a.active = active;
     a.n_active = n_active;

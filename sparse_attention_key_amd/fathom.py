@@ -45,21 +45,22 @@ def lib() -> ctypes.CDLL:
         L.fathom_abi_version.argtypes, L.fathom_abi_version.restype = [], ctypes.c_int
         L.fathom_strerror.argtypes, L.fathom_strerror.restype = [ctypes.c_int], ctypes.c_char_p
         L.fathom_pack.argtypes = [P, i32, i32, i64, i32, P, P, P, P]
+        L.fathom_pack_range.argtypes = [P, i32, i32, i64, i64, i32, P, P, P, i64, P]
         L.fathom_plan.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P]
-        L.fathom_scan.argtypes = [P, P, i32, i32, i64, P, P, P, P, i32, P, P]
+        L.fathom_scan.argtypes = [P, P, i32, i32, i64, i64, P, P, P, P, i32, P, P]
         L.fathom_topk_workspace_bytes.argtypes = [i32, i32, i64, i32]
         L.fathom_topk_workspace_bytes.restype = sz
         L.fathom_topk.argtypes = [P, i32, i32, i64, i32, P, P, P, P, P, sz, P]
         L.fathom_scan_topk_workspace_bytes.argtypes = [i32, i32, i64, i32]
         L.fathom_scan_topk_workspace_bytes.restype = sz
-        L.fathom_scan_topk.argtypes = [P, P, i32, i32, i64, P, P, P, P, i32, i32, P, P, P, P, P, sz, P]
+        L.fathom_scan_topk.argtypes = [P, P, i32, i32, i64, i64, P, P, P, P, i32, i32, P, P, P, P, P, sz, P]
         L.fathom_scan_topk_stage.argtypes = [i32] + L.fathom_scan_topk.argtypes
         L.fathom_read_probe.argtypes = [P, sz, P, P]
         L.fathom_gather_rows.argtypes = [P, i64, i64, i64, i32, P, P, i32, P, P]
         L.fathom_gather_rows.restype = ctypes.c_int
         L.fathom_read_probe.restype = ctypes.c_int
-        for f in (L.fathom_pack, L.fathom_plan, L.fathom_scan, L.fathom_topk, L.fathom_scan_topk,
-                  L.fathom_scan_topk_stage):
+        for f in (L.fathom_pack, L.fathom_pack_range, L.fathom_plan, L.fathom_scan, L.fathom_topk,
+                  L.fathom_scan_topk, L.fathom_scan_topk_stage):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -95,6 +96,16 @@ def nblocks(n: int) -> int:
     return (n + 63) // 64
 
 
+def _nb_cap(planes, nb_cap):
+    """Blocks per index row: given, else the last dimension of a [P][D][4][L]
+    planes tensor, else 0 (a dense index)."""
+    if nb_cap is not None:
+        return int(nb_cap)
+    if isinstance(planes, torch.Tensor) and planes.dim() == 4:
+        return int(planes.shape[-1])
+    return 0
+
+
 # ------------------------------------------------------------------- pack
 
 def pack_into(keys, planes, scales, rot=None, stream=None):
@@ -104,6 +115,17 @@ def pack_into(keys, planes, scales, rot=None, stream=None):
     dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[keys.dtype]
     _check("fathom_pack", lib().fathom_pack(_ptr(keys), dt, P, n, D, _ptr(rot), _ptr(planes),
                                             _ptr(scales), _stream(stream)))
+
+
+def pack_range(keys, tok0: int, planes, scales, rot=None, stream=None):
+    """Pack keys [P][m][D] as tokens tok0 .. tok0+m-1 (tok0 a multiple of 64)
+    into an index planes [P][D][4][nb_cap], scales [P][D][nb_cap]; other
+    blocks are left as they are (appends repack the tail block)."""
+    P, m, D = keys.shape
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[keys.dtype]
+    _check("fathom_pack_range", lib().fathom_pack_range(
+        _ptr(keys), dt, P, int(tok0), m, D, _ptr(rot), _ptr(planes), _ptr(scales),
+        int(planes.shape[-1]), _stream(stream)))
 
 
 def pack(keys, rot=None, stream=None):
@@ -144,16 +166,16 @@ def plan(q, sigma2, budget: int, mode: int = PLAN_WATERFILL, rot=None, stream=No
 
 # ------------------------------------------------------------------- scan
 
-def scan_into(planes, scales, n: int, pl: Plan, scores, stream=None):
+def scan_into(planes, scales, n: int, pl: Plan, scores, stream=None, nb_cap=None):
     P, D = pl.P, pl.D
     _check("fathom_scan", lib().fathom_scan(
-        _ptr(planes), _ptr(scales), P, D, int(n), _ptr(pl.depth), _ptr(pl.active), _ptr(pl.n_active),
-        _ptr(pl.q_used), pl.G, _ptr(scores), _stream(stream)))
+        _ptr(planes), _ptr(scales), P, D, int(n), _nb_cap(planes, nb_cap), _ptr(pl.depth),
+        _ptr(pl.active), _ptr(pl.n_active), _ptr(pl.q_used), pl.G, _ptr(scores), _stream(stream)))
 
 
-def scan(planes, scales, n: int, pl: Plan, stream=None):
+def scan(planes, scales, n: int, pl: Plan, stream=None, nb_cap=None):
     scores = torch.empty((pl.P, pl.G, nblocks(n) * 64), dtype=torch.float32, device=pl.q_used.device)
-    scan_into(planes, scales, n, pl, scores, stream)
+    scan_into(planes, scales, n, pl, scores, stream, nb_cap)
     return scores
 
 
@@ -195,25 +217,28 @@ def topk(scores, n: int, k: int, stream=None) -> TopkOut:
 
 # ------------------------------------------------------- fused scan + top-k
 
-def scan_topk_into(planes, scales, n: int, pl: Plan, out: TopkOut, stream=None):
+def scan_topk_into(planes, scales, n: int, pl: Plan, out: TopkOut, stream=None, nb_cap=None):
     """Scores, top-k and union of every pair without materialising scores;
     `out` must be a TopkOut(..., fused=True)."""
     _check("fathom_scan_topk", lib().fathom_scan_topk(
-        _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _ptr(pl.depth), _ptr(pl.active),
+        _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _nb_cap(planes, nb_cap), _ptr(pl.depth),
+        _ptr(pl.active),
         _ptr(pl.n_active), _ptr(pl.q_used), pl.G, out.k, _ptr(out.idx), _ptr(out.val), _ptr(out.union),
         _ptr(out.union_len), _ptr(out.ws), out.ws.numel(), _stream(stream)))
     return out
 
 
-def scan_topk(planes, scales, n: int, pl: Plan, k: int, stream=None) -> TopkOut:
+def scan_topk(planes, scales, n: int, pl: Plan, k: int, stream=None, nb_cap=None) -> TopkOut:
     out = TopkOut(pl.P, pl.G, n, k, pl.q_used.device, fused=True)
-    return scan_topk_into(planes, scales, n, pl, out, stream)
+    return scan_topk_into(planes, scales, n, pl, out, stream, nb_cap)
 
 
-def scan_topk_stage(stage: int, planes, scales, n: int, pl: Plan, out: TopkOut, stream=None):
+def scan_topk_stage(stage: int, planes, scales, n: int, pl: Plan, out: TopkOut, stream=None,
+                    nb_cap=None):
     """One stage (1 threshold, 2 filtered scan, 3 select + union) of scan_topk_into."""
     _check("fathom_scan_topk_stage", lib().fathom_scan_topk_stage(
-        int(stage), _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _ptr(pl.depth), _ptr(pl.active),
+        int(stage), _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _nb_cap(planes, nb_cap),
+        _ptr(pl.depth), _ptr(pl.active),
         _ptr(pl.n_active), _ptr(pl.q_used), pl.G, out.k, _ptr(out.idx), _ptr(out.val), _ptr(out.union),
         _ptr(out.union_len), _ptr(out.ws), out.ws.numel(), _stream(stream)))
     return out

@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.fathom_abi_version() == 1
+    assert L.fathom_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.fathom_strerror(code)
     assert L.fathom_strerror(-99) == b"unknown status"
@@ -59,22 +59,40 @@ def test_plan_validation(L):
 
 
 def test_scan_validation(L):
-    base = [A, A, 1, 128, 4096, A, A, A, A, 4, A, None]
-    bad = list(base)
-    bad[10] = None
-    assert L.fathom_scan(*bad) == F.ERR_ARG
-    bad = list(base)
-    bad[9] = 9
-    assert L.fathom_scan(*bad) == F.ERR_SHAPE
-    bad = list(base)
-    bad[4] = 0
-    assert L.fathom_scan(*bad) == F.ERR_SHAPE
-    bad = list(base)
-    bad[2] = 65536
-    assert L.fathom_scan(*bad) == F.ERR_SHAPE
-    bad = list(base)
-    bad[0] = MIS
-    assert L.fathom_scan(*bad) == F.ERR_ALIGN
+    # planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, scores, stream
+    base = [A, A, 1, 128, 4096, 0, A, A, A, A, 4, A, None]
+
+    def with_(i, v):
+        b = list(base)
+        b[i] = v
+        return b
+    assert L.fathom_scan(*with_(11, None)) == F.ERR_ARG
+    assert L.fathom_scan(*with_(10, 9)) == F.ERR_SHAPE
+    assert L.fathom_scan(*with_(4, 0)) == F.ERR_SHAPE
+    assert L.fathom_scan(*with_(2, 65536)) == F.ERR_SHAPE
+    assert L.fathom_scan(*with_(5, 63)) == F.ERR_SHAPE       # 4096 tokens need 64 blocks per row
+    assert L.fathom_scan(*with_(5, -1)) == F.ERR_SHAPE
+    assert L.fathom_scan(*with_(5, 1 << 26)) == F.ERR_SHAPE
+    assert L.fathom_scan(*with_(0, MIS)) == F.ERR_ALIGN
+
+
+def test_pack_range_validation(L):
+    # keys, dtype, P, tok0, m, D, rot, planes, scales, nb_cap, stream
+    base = [A, 0, 2, 128, 10, 128, None, A, A, 4, None]
+
+    def with_(i, v):
+        b = list(base)
+        b[i] = v
+        return b
+    assert L.fathom_pack_range(*with_(0, None)) == F.ERR_ARG
+    assert L.fathom_pack_range(*with_(1, 5)) == F.ERR_ARG
+    assert L.fathom_pack_range(*with_(3, 100)) == F.ERR_ARG   # not a block boundary
+    assert L.fathom_pack_range(*with_(3, -64)) == F.ERR_ARG
+    assert L.fathom_pack_range(*with_(4, 0)) == F.ERR_SHAPE
+    assert L.fathom_pack_range(*with_(4, 200)) == F.ERR_SHAPE  # past the 4-block capacity
+    assert L.fathom_pack_range(*with_(9, 2)) == F.ERR_SHAPE
+    assert L.fathom_pack_range(*with_(5, 129)) == F.ERR_SHAPE
+    assert L.fathom_pack_range(*with_(7, MIS)) == F.ERR_ALIGN
 
 
 def test_topk_validation(L):

@@ -9,6 +9,7 @@ import zlib
 
 import numpy as np
 import pytest
+import torch
 
 import workloads as wl
 from tests.gpu_util import bf16_dev, dev, need_gpu, say, score_tol, u16, u64
@@ -372,3 +373,80 @@ def test_gather_rows_bit_exact(F, orc, shared, host):
     assert np.array_equal(got, ref)
     if ph is not None:
         ph.free()
+
+
+# ------------------------------------------------------- appends (pack_range)
+
+SENTINEL = -0x0123456789ABCDF  # marks index words no call may touch
+
+
+def _cap_index(P, D, cap, device="cuda"):
+    planes = torch.full((P, D, 4, cap), SENTINEL, dtype=torch.int64, device=device)
+    scales = torch.full((P, D, cap), -1, dtype=torch.int16, device=device)
+    return planes, scales
+
+
+def test_append_token_by_token_matches_full_pack(F, orc):
+    P, D, n0, n1, cap = 3, 128, 600, 1000, 20  # 1000 tokens fill 16 blocks of a 20-block capacity
+    g = np.random.default_rng(41)
+    x = [wl.to_bf16_exact((g.standard_normal((n1, D)) * np.exp(0.8 * g.standard_normal(D))).astype(np.float32))
+         for _ in range(P)]
+    xd = bf16_dev(np.stack(x))
+    say("append", P, n0, "->", n1, "capacity", cap)
+    planes, scales = _cap_index(P, D, cap)
+    F.pack_range(xd[:, :n0].contiguous(), 0, planes, scales)
+    for t in range(n0, n1):  # token t arrives: repack its block from that block's raw keys
+        tok0 = (t // 64) * 64
+        F.pack_range(xd[:, tok0:t + 1].contiguous(), tok0, planes, scales)
+    torch.cuda.synchronize()
+    nb = (n1 + 63) // 64
+    got_p, got_s = u64(planes), u16(scales)
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        assert np.array_equal(got_p[p][:, :, :nb], rp), p
+        assert np.array_equal(got_s[p][:, :nb], rs), p
+    assert np.all(planes[:, :, :, nb:].cpu().numpy() == SENTINEL)
+    assert np.all(scales[:, :, nb:].cpu().numpy() == -1)
+
+
+def test_pack_range_offset_and_rotation(F, orc):
+    P, D, n, cap = 2, 128, 700, 16
+    g = np.random.default_rng(42)
+    x = [g.standard_normal((n, D)).astype(np.float32) * 3 for _ in range(P)]
+    rot = np.stack([np.linalg.qr(g.standard_normal((D, D)))[0].astype(np.float32) for _ in range(P)])
+    say("pack_range offset 128, 300 tokens, rotated")
+    planes, scales = _cap_index(P, D, cap)
+    F.pack_range(dev(np.stack(x))[:, 128:428].contiguous(), 128, planes, scales, rot=dev(rot))
+    torch.cuda.synchronize()
+    got_p, got_s = u64(planes), u16(scales)
+    for p in range(P):
+        # blocks 2..6 hold tokens 128..427; block 6 is partial (tokens 384..427)
+        rp, rs = orc.pack(x[p][128:428], rot=rot[p])
+        assert np.array_equal(got_p[p][:, :, 2:7], rp), p
+        assert np.array_equal(got_s[p][:, 2:7], rs), p
+    assert np.all(planes[:, :, :, :2].cpu().numpy() == SENTINEL)
+    assert np.all(planes[:, :, :, 7:].cpu().numpy() == SENTINEL)
+
+
+def test_scan_topk_on_capacity_index(F, orc):
+    P, D, G, n, cap, budget, k = 3, 128, 4, 5000, 100, 48, 256
+    g = np.random.default_rng(43)
+    x = [(g.standard_normal((n, D)) * np.exp(0.7 * g.standard_normal(D))).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, n + 3)
+    say("scan+top-k on a capacity index", n, cap)
+    xd = dev(np.stack(x))
+    planes, scales = _cap_index(P, D, cap)
+    F.pack_range(xd, 0, planes, scales)
+    dense_p, dense_s = F.pack(xd)
+    pl = F.plan(dev(q), dev(s2), budget)
+    out = F.scan_topk(planes, scales, n, pl, k)
+    ref_out = F.scan_topk(dense_p, dense_s, n, pl, k)
+    scores = F.scan(planes, scales, n, pl)
+    ref_scores = F.scan(dense_p, dense_s, n, pl)
+    assert torch.equal(out.idx, ref_out.idx) and torch.equal(out.union, ref_out.union)
+    assert torch.equal(scores.view(torch.int32), ref_scores.view(torch.int32))
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        ref = orc.step(rp, rs, n, q[p], s2[p], budget, k)
+        assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"]), p
+        assert np.array_equal(out.union[p].cpu().numpy(), ref["union"]), p
