@@ -103,21 +103,58 @@ def build_index(F, w, device):
     return planes, scales
 
 
-def inputs(w):
-    """Queries, and the calibration statistics: per-channel variances, or for
-    rotated storage the KLT basis and the variances of the rotated coordinates."""
+def inputs(F, w, device):
+    """Queries, and the calibration statistics computed on the device from
+    each pair's calibration sample: per-channel variances, or for rotated
+    storage the KLT basis and the variances of the rotated coordinates.
+    Returns q (numpy), s2 and rot (device tensors) and the calibration time."""
+    import torch
+
     import workloads as wl
-    from sparse_attention_key_amd import calib
 
     q = np.stack([wl.queries(w, p) for p in range(w.P)])
-    if not w.rotated:
-        s2 = np.stack([calib.channel_variance(wl.calibration_sample(w, p)) for p in range(w.P)])
-        return q, s2, None
-    rots, lams = zip(*(calib.rotation(wl.calibration_sample(w, p)) for p in range(w.P)))
-    return q, np.stack(lams), np.stack(rots)
+    keys = torch.from_numpy(np.stack([wl.calibration_sample(w, p) for p in range(w.P)])).to(device)
+    cov, s2 = F.calib_covariance(keys, with_cov=w.rotated)
+    rot = None
+    if w.rotated:
+        rot, s2 = F.calib_basis(cov)
+    torch.cuda.synchronize()
+    calib = calib_probe(F, keys, w.rotated)
+    del keys, cov
+    return q, s2, rot, calib
 
 
-def build_host_index(F, w, rot_np, device):
+def calib_probe(F, keys, basis: bool, reps: int = 3):
+    """Device time of the calibration statistics for these keys [P][m][D]
+    (covariance, and the eigenbasis when the storage is rotated), and of the
+    per-KV-head statistics from a session's own prefill: one layer's 8 KV
+    heads x 102,400 keys, covariance alone and with the eigenbasis."""
+    import torch
+
+    def timed(k, with_basis):
+        F.calib_covariance(k, with_cov=with_basis)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            cov, _ = F.calib_covariance(k, with_cov=with_basis)
+            if with_basis:
+                F.calib_basis(cov)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"pairs": int(keys.shape[0]), "keys_per_pair": int(keys.shape[1]), "basis": bool(basis),
+           "ms": round(timed(keys, basis), 3)}
+    g = torch.Generator(device=keys.device).manual_seed(20260915)
+    pre = (torch.randn((8, 102400, keys.shape[2]), device=keys.device, generator=g)).to(torch.bfloat16)
+    out["prefill_8x102400_cov_ms"] = round(timed(pre, False), 3)
+    out["prefill_8x102400_cov_basis_ms"] = round(timed(pre, True), 3)
+    del pre
+    return out
+
+
+def build_host_index(F, w, rot, device):
     """Keys drawn on the GPU, rotated into the calibration basis (a float32
     GEMM of the input generator side), packed on the GPU chunk by chunk and
     copied into mapped pinned host memory."""
@@ -142,7 +179,7 @@ def build_host_index(F, w, rot_np, device):
         keys = wl.keys_device(w, pairs, device=device)
         y = torch.empty((len(pairs), w.n, w.D), dtype=torch.float32, device=device)
         for i, p in enumerate(pairs):
-            y[i] = keys[i].float() @ torch.from_numpy(rot_np[p]).to(device)
+            y[i] = keys[i].float() @ rot[p]
         del keys
         F.pack_into(y, planes[: len(pairs)], scales[: len(pairs)])
         del y
@@ -259,10 +296,11 @@ def append_probe(F, w, planes, scales, device):
     return {"pairs": w.P, "tokens_in_block": m, "us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2)}
 
 
-def cpu_baseline(w, q, s2, budget, mode, pairs, threads, rot=None):
+def cpu_baseline(w, q, budget, mode, pairs, threads):
     """Time the CPU oracle (as it stands) on a bounded sample of pairs: the
     same plan + scores + top-k + union per pair, run `threads` pairs at a
-    time; scaled to a whole step of all pairs."""
+    time; scaled to a whole step of all pairs.  Its calibration statistics
+    come from the oracle, on the same calibration samples."""
     import oracle
     import workloads as wl
 
@@ -270,6 +308,14 @@ def cpu_baseline(w, q, s2, budget, mode, pairs, threads, rot=None):
 
     pairs = min(pairs, w.P)
     sel = [int(p) for p in np.linspace(0, w.P - 1, pairs).round()]
+    s2, rot = {}, None
+    if w.rotated:
+        rot = {}
+        for p in sel:
+            rot[p], s2[p] = oracle.calib.klt_basis(wl.calibration_sample(w, p))
+    else:
+        for p in sel:
+            s2[p] = oracle.calib.channel_variance(wl.calibration_sample(w, p))
     packed = {}
     t0 = time.time()
     keys = {p: wl.keys_device(w, [p])[0].float().cpu().numpy() for p in sel}  # generator output
@@ -319,12 +365,12 @@ def main():
     dev = torch.device("cuda:0")
     F.lib()
     log(f"workload {w.name}: P={w.P} n={w.n} G={w.G} D={w.D} B={budget} k={w.k} mode={a.mode}")
-    q_np, s2_np, rot_np = inputs(w)
-    log("calibration + queries ready")
+    q_np, s2, rot, calib = inputs(F, w, dev)
+    log(f"calibration on the device: {calib}")
     host = None
     link = {}
     if w.host_resident:
-        host = build_host_index(F, w, rot_np, dev)
+        host = build_host_index(F, w, rot, dev)
         planes, scales = host[0].dev, host[1].dev  # device addresses of mapped host memory
         link = link_probes(F, host[0], dev)
         log(f"host link: {link}")
@@ -333,8 +379,6 @@ def main():
         link = {"hbm_read_probe": hbm_probe(F, planes, dev)}
         log(f"HBM streaming read of the index: {link['hbm_read_probe']} GB/s")
     q = torch.from_numpy(q_np).to(dev)
-    s2 = torch.from_numpy(s2_np).to(dev)
-    rot = None if rot_np is None else torch.from_numpy(rot_np).to(dev)
     pl = F.Plan(w.P, w.G, w.D, dev)
     npad = w.nb * 64
     out = F.TopkOut(w.P, w.G, w.n, w.k, dev, fused=True)
@@ -443,6 +487,7 @@ def main():
         "keys_per_s": round(w.P * w.n / (ms_step * 1e-3), 1),
         "bits_per_token": round(bits_tok, 2), "active_channels_mean": round(float(act.double().mean()), 2),
         "roofline": roof,
+        "calibration": calib,
     }
     if host is not None:
         for h in host:
@@ -454,8 +499,7 @@ def main():
         res["append"] = append_probe(F, w, planes, scales, dev)
         log(f"append (repack the last block of every pair): {res['append']}")
     if a.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, q_np, s2_np, budget, a.mode, a.cpu_pairs, a.cpu_threads,
-                                           rot=rot_np)
+        res["cpu_baseline"] = cpu_baseline(w, q_np, budget, a.mode, a.cpu_pairs, a.cpu_threads)
     print(json.dumps(res), flush=True)
 
 

@@ -254,6 +254,43 @@ int fathom_gather_rows(const void* table, int64_t table_rows, int64_t row_bytes,
                        const int32_t* union_len, int32_t cap, void* out, void* stream);
 
 /*
+ * fathom_calib_covariance -- calibration statistics of each pair on the
+ * device: the water-filling weights are the variances of the stored
+ * coordinates, and the rotated storage is the eigenbasis of the key
+ * covariance (reverse water-filling and basis-choice sections).  The
+ * calibration-domain passage computes them from the session's own prefill
+ * keys, one covariance per KV head.
+ *
+ *   keys  [P][m][D]  float32 (F32) or bfloat16 (BF16), m >= 1
+ *   cov   [P][D][D]  float64 centred population covariance
+ *                    sum_t (x_t - mu)(x_t - mu)^T / m, or NULL
+ *   var   [P][D]     float32 channel variances (cov's diagonal rounded once),
+ *                    or NULL; at least one of cov and var must be given
+ *   ws    device workspace of fathom_calib_workspace_bytes(P, m, D) bytes
+ * Accumulation is float64 in a fixed order (deterministic).  Errors:
+ * ERR_ARG, ERR_SHAPE, ERR_WORKSPACE, ERR_ALIGN.
+ */
+size_t fathom_calib_workspace_bytes(int32_t P, int64_t m, int32_t D);
+int fathom_calib_covariance(const void* keys, int32_t dtype, int32_t P, int64_t m, int32_t D,
+                            double* cov, float* var, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fathom_calib_basis -- eigen-decomposition of each pair's covariance by
+ * cyclic Jacobi rotations (float64 matrix, float32 eigenvectors), one
+ * workgroup per pair.
+ *
+ *   cov  [P][D][D] float64 symmetric (from fathom_calib_covariance)
+ *   U    [P][D][D] float32: column c is the eigenvector of the c-th largest
+ *                  eigenvalue, signed so that its largest-magnitude component
+ *                  is positive -- the rot argument of fathom_pack/plan
+ *   lam  [P][D]    float32 eigenvalues in descending order, clamped at 0: the
+ *                  variances of the rotated coordinates (sigma2 of fathom_plan)
+ * Sweeps stop when the off-diagonal norm falls below 1e-12 of the diagonal
+ * norm (at most 20).  Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN.
+ */
+int fathom_calib_basis(const double* cov, int32_t P, int32_t D, float* U, float* lam, void* stream);
+
+/*
  * fathom_read_probe -- measurement utility, not a step of the method: reads
  * `bytes` (rounded down to a multiple of 16) from `src` once with 16-byte
  * coalesced loads and folds them into sink[0..1023] (caller-owned device

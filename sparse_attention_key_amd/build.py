@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfathom.so")
-SOURCES = ["api.hip", "pack.hip", "plan.hip", "scan.hip", "topk.hip", "probe.hip", "gather.hip"]
+SOURCES = ["api.hip", "pack.hip", "plan.hip", "scan.hip", "topk.hip", "probe.hip", "gather.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -237,6 +237,33 @@ int fathom_gather_rows(const void* table, int64_t table_rows, int64_t row_bytes,
                                     union_len, cap, out, (hipStream_t)stream));
 }
 
+size_t fathom_calib_workspace_bytes(int32_t P, int64_t m, int32_t D)
+{
+    if (P < 1 || P > kMaxPairs || m < 1 || m > kMaxTokens || D < 1 || D > kMaxD) return 0;
+    return calib_workspace_bytes(P, m, D);
+}
+
+int fathom_calib_covariance(const void* keys, int32_t dtype, int32_t P, int64_t m, int32_t D,
+                            double* cov, float* var, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!keys || (!cov && !var)) return FATHOM_ERR_ARG;
+    if (dtype != FATHOM_DTYPE_F32 && dtype != FATHOM_DTYPE_BF16) return FATHOM_ERR_ARG;
+    int s = check_shape(P, m, D);
+    if (s) return s;
+    if (!ws || ws_bytes < calib_workspace_bytes(P, m, D)) return FATHOM_ERR_WORKSPACE;
+    if (!aligned16(keys) || !aligned16(ws) || (cov && !aligned16(cov)) || (var && !aligned16(var)))
+        return FATHOM_ERR_ALIGN;
+    return hip_status(launch_calib_covariance(keys, dtype, P, m, D, cov, var, ws, (hipStream_t)stream));
+}
+
+int fathom_calib_basis(const double* cov, int32_t P, int32_t D, float* U, float* lam, void* stream)
+{
+    if (!cov || !U || !lam) return FATHOM_ERR_ARG;
+    if (P < 1 || P > kMaxPairs || D < 1 || D > kMaxD) return FATHOM_ERR_SHAPE;
+    if (!aligned16(cov) || !aligned16(U) || !aligned16(lam)) return FATHOM_ERR_ALIGN;
+    return hip_status(launch_calib_basis(cov, P, D, U, lam, (hipStream_t)stream));
+}
+
 int fathom_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream)
 {
     if (!src || !sink || bytes < 16) return FATHOM_ERR_ARG;

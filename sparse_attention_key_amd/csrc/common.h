@@ -141,6 +141,11 @@ hipError_t launch_gather(const void* table, int64_t table_rows, int64_t row_byte
                          int cap, void* out, hipStream_t st);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 
+size_t calib_workspace_bytes(int P, int64_t m, int D);
+hipError_t launch_calib_covariance(const void* keys, int dtype, int P, int64_t m, int D, double* cov,
+                                   float* var, void* ws, hipStream_t st);
+hipError_t launch_calib_basis(const double* cov, int P, int D, float* U, float* lam, hipStream_t st);
+
 struct TopkLayout {
     int64_t m;           // selections = P * G
     int64_t stride;      // sample one run of 32 blocks in every `stride` runs

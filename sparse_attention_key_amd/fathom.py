@@ -58,6 +58,12 @@ def lib() -> ctypes.CDLL:
         L.fathom_read_probe.argtypes = [P, sz, P, P]
         L.fathom_gather_rows.argtypes = [P, i64, i64, i64, i32, P, P, i32, P, P]
         L.fathom_gather_rows.restype = ctypes.c_int
+        L.fathom_calib_workspace_bytes.argtypes = [i32, i64, i32]
+        L.fathom_calib_workspace_bytes.restype = sz
+        L.fathom_calib_covariance.argtypes = [P, i32, i32, i64, i32, P, P, P, sz, P]
+        L.fathom_calib_covariance.restype = ctypes.c_int
+        L.fathom_calib_basis.argtypes = [P, i32, i32, P, P, P]
+        L.fathom_calib_basis.restype = ctypes.c_int
         L.fathom_read_probe.restype = ctypes.c_int
         for f in (L.fathom_pack, L.fathom_pack_range, L.fathom_plan, L.fathom_scan, L.fathom_topk,
                   L.fathom_scan_topk, L.fathom_scan_topk_stage):
@@ -258,3 +264,35 @@ def gather_rows(table, table_rows: int, row_bytes: int, pair_stride_rows: int, u
         _ptr(table), int(table_rows), int(row_bytes), int(pair_stride_rows), P, _ptr(union),
         _ptr(union_len), cap, _ptr(out), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------ calibration
+
+def calib_workspace_bytes(P: int, m: int, D: int) -> int:
+    return int(lib().fathom_calib_workspace_bytes(P, int(m), D))
+
+
+def calib_covariance(keys, with_cov: bool = True, stream=None):
+    """keys [P][m][D] float32|bfloat16 (calibration or prefill keys) ->
+    (cov [P][D][D] float64 centred population covariance or None,
+     var [P][D] float32 channel variances)."""
+    P, m, D = keys.shape
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[keys.dtype]
+    cov = torch.empty((P, D, D), dtype=torch.float64, device=keys.device) if with_cov else None
+    var = torch.empty((P, D), dtype=torch.float32, device=keys.device)
+    nbytes = calib_workspace_bytes(P, m, D)
+    ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=keys.device)
+    _check("fathom_calib_covariance", lib().fathom_calib_covariance(
+        _ptr(keys), dt, P, int(m), D, _ptr(cov), _ptr(var), _ptr(ws), ws.numel(), _stream(stream)))
+    return cov, var
+
+
+def calib_basis(cov, stream=None):
+    """cov [P][D][D] float64 -> (U [P][D][D] float32, columns the eigenvectors
+    by descending eigenvalue, lam [P][D] float32 eigenvalues clamped at 0)."""
+    P, D, _ = cov.shape
+    U = torch.empty((P, D, D), dtype=torch.float32, device=cov.device)
+    lam = torch.empty((P, D), dtype=torch.float32, device=cov.device)
+    _check("fathom_calib_basis", lib().fathom_calib_basis(_ptr(cov), P, D, _ptr(U), _ptr(lam),
+                                                          _stream(stream)))
+    return U, lam

@@ -132,3 +132,23 @@ def test_gather_validation(L):
     ok[4] = 65536
     assert L.fathom_gather_rows(*ok) == F.ERR_SHAPE
     assert L.fathom_gather_rows(*args(t=MIS)) == F.ERR_ALIGN
+
+
+def test_calib_validation(L):
+    ws = L.fathom_calib_workspace_bytes(2, 5000, 128)
+    assert ws > 0
+    assert L.fathom_calib_workspace_bytes(0, 5000, 128) == 0
+    assert L.fathom_calib_workspace_bytes(2, 5000, 129) == 0
+    args = lambda **kw: [kw.get("k", A), kw.get("dt", 1), 2, kw.get("m", 5000), 128, kw.get("cov", A),
+                         kw.get("var", A), kw.get("ws", A), kw.get("wsb", ws), None]
+    assert L.fathom_calib_covariance(*args(k=None)) == F.ERR_ARG
+    assert L.fathom_calib_covariance(*args(cov=None, var=None)) == F.ERR_ARG
+    assert L.fathom_calib_covariance(*args(dt=3)) == F.ERR_ARG
+    assert L.fathom_calib_covariance(*args(m=0)) == F.ERR_SHAPE
+    assert L.fathom_calib_covariance(*args(wsb=ws - 1)) == F.ERR_WORKSPACE
+    assert L.fathom_calib_covariance(*args(ws=None)) == F.ERR_WORKSPACE
+    assert L.fathom_calib_covariance(*args(cov=MIS)) == F.ERR_ALIGN
+    assert L.fathom_calib_basis(None, 2, 128, A, A, None) == F.ERR_ARG
+    assert L.fathom_calib_basis(A, 2, 129, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_calib_basis(A, 0, 128, A, A, None) == F.ERR_SHAPE
+    assert L.fathom_calib_basis(MIS, 2, 128, A, A, None) == F.ERR_ALIGN

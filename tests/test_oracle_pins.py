@@ -419,3 +419,30 @@ def test_gather_rows_definition(orc):
     assert np.array_equal(out[1, :4], table[:4]) and np.all(out[1, 4:] == -1)
     rep = orc.gather_rows(np.stack([table, table]), idx, lens, init)
     assert np.array_equal(out, rep)
+
+
+# ------------------------------------------------------------ calibration
+
+def test_channel_variance_closed_form(orc):
+    # every channel j takes the values mu_j + a_j and mu_j - a_j equally often:
+    # centred population variance a_j^2 exactly, whatever the mean
+    D = 16
+    a = np.arange(1, D + 1, dtype=np.float64) * 0.25
+    mu = np.linspace(-40.0, 40.0, D)
+    x = np.concatenate([mu + a, mu - a, mu - a, mu + a])[None].reshape(4, D)
+    v = orc.calib.channel_variance(x)
+    assert np.array_equal(v, (a * a).astype(np.float32))
+
+
+def test_klt_basis_recovers_a_constructed_covariance(orc):
+    # rows +-sqrt(D) s_i q_i (i < D) have mean 0 and covariance Q diag(s^2) Q^T,
+    # so the basis must be Q (up to signs) with eigenvalues s^2, descending
+    D = 24
+    g = np.random.default_rng(5)
+    Q = np.linalg.qr(g.standard_normal((D, D)))[0]
+    s = np.linspace(3.0, 0.1, D)
+    rows = [sign * np.sqrt(D) * s[i] * Q[:, i] for i in range(D) for sign in (1.0, -1.0)]
+    U, lam = orc.calib.klt_basis(np.array(rows))
+    assert np.allclose(lam, s * s, rtol=1e-6)
+    assert np.allclose(np.abs(np.sum(U * Q, axis=0)), 1.0, atol=1e-6)
+    assert np.all(np.diff(lam) <= 0)
