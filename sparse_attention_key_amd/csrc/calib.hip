@@ -150,8 +150,9 @@ __device__ __forceinline__ int rr_index(int r, int k, int Dp)
 }
 
 constexpr int kJacobiSweeps = 20;
+constexpr int kJacobiThreads = 1024;
 
-__global__ __launch_bounds__(256) void jacobi_kernel(const double* __restrict__ cov, int D,
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __restrict__ cov, int D,
                                                      float* __restrict__ U, float* __restrict__ lam)
 {
     extern __shared__ double s_dyn[];
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const double* __restrict__ 
     float* V = (float*)(s_dyn + ntri);       // Dp x Dp, row-major: V[row][col]
     __shared__ double s_c[kMaxD / 2], s_s[kMaxD / 2];
     __shared__ int s_i[kMaxD / 2], s_j[kMaxD / 2];
-    __shared__ double s_red[256 / kWave * 2];
+    __shared__ double s_red[kJacobiThreads / kWave * 2];
     __shared__ int s_rank[kMaxD];
     const int p = blockIdx.x;
     const double* C = cov + (size_t)p * D * D;
@@ -221,10 +222,27 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const double* __restrict__ 
                 s_j[k] = j;
             }
             __syncthreads();
-            // A <- J^T A J: every 2 x 2 block (pair x, pair y), x <= y, on its own
-            for (int b = threadIdx.x; b < half * half; b += blockDim.x) {
-                const int x = b / half, y = b - x * half;
-                if (y < x) continue;  // the symmetric block (y, x) is the same storage
+            // A <- J^T A J: every 2 x 2 block (pair x, pair y), x <= y, on its
+            // own.  The half*(half+1)/2 blocks are enumerated by folding row
+            // r of the triangle (half - r blocks) with row half-1-r (r + 1
+            // blocks) into one row of half + 1 (half is even when D > 2).
+            const int wrow = half + 1;
+            const int nblk = (half / 2) * wrow + (half & 1) * ((half + 1) / 2);
+            for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
+                int x, y;
+                const int r = b / wrow, c = b - r * wrow;
+                if (r < half / 2) {
+                    if (c < half - r) {
+                        x = r;
+                        y = r + c;
+                    } else {
+                        x = half - 1 - r;
+                        y = x + (c - (half - r));
+                    }
+                } else {  // odd half: the middle row alone
+                    x = half / 2;
+                    y = x + c;
+                }
                 const int xi = s_i[x], xj = s_j[x], yi = s_i[y], yj = s_j[y];
                 const double cx = s_c[x], sx = s_s[x], cy = s_c[y], sy = s_s[y];
                 if (x == y) {
@@ -324,7 +342,7 @@ hipError_t launch_calib_basis(const double* cov, int P, int D, float* U, float* 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    jacobi_kernel<<<dim3((unsigned)P), 256, dyn, st>>>(cov, D, U, lam);
+    jacobi_kernel<<<dim3((unsigned)P), kJacobiThreads, dyn, st>>>(cov, D, U, lam);
     return hipGetLastError();
 }
 
