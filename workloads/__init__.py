@@ -7,7 +7,8 @@ both be fed from it.
 
 Every stream is numpy PCG64 seeded with SeedSequence([20260915, layer,
 kv_head, stream]), streams 0 = channel scales, 1 = keys, 2 = queries,
-3 = planted positions, 4 = calibration sample, 5 = mixing matrix.  Large key
+3 = planted positions, 4 = calibration sample, 5 = mixing matrix,
+6 = values (for attention-output error measurements).  Large key
 tensors (131k and 1M tokens x 288 pairs) are drawn on the GPU with torch's
 Philox generator seeded from the same SeedSequence; small ones on the host.
 
@@ -22,7 +23,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BASE_SEED = 20260915
-S_SCALES, S_KEYS, S_QUERIES, S_PLANTED, S_CALIB, S_MIX = range(6)
+S_SCALES, S_KEYS, S_QUERIES, S_PLANTED, S_CALIB, S_MIX, S_VALUES = range(7)
 CALIB_KEYS = 8192
 
 
@@ -160,6 +161,15 @@ def planted_positions(w: Workload, p: int, n: int | None = None) -> np.ndarray:
     n = w.n if n is None else n
     layer, kv = w.pair(p)
     return rng(layer, kv, S_PLANTED).choice(n, w.G * w.planted, replace=False).reshape(w.G, w.planted)
+
+
+def values_host(w: Workload, p: int, n: int | None = None) -> np.ndarray:
+    """Values of one pair, [n][D] float32 N(0, 1) (bf16-exact for bf16
+    workloads): only used to measure attention-output error."""
+    n = w.n if n is None else n
+    layer, kv = w.pair(p)
+    v = rng(layer, kv, S_VALUES).standard_normal((n, w.D), dtype=np.float32)
+    return to_bf16_exact(v) if w.key_dtype == "bf16" else v
 
 
 def calibration_sample(w: Workload, p: int) -> np.ndarray:
