@@ -335,13 +335,10 @@ hipError_t launch_calib_basis(const double* cov, int P, int D, float* U, float* 
 {
     const int Dp = (D + 1) & ~1;
     const size_t dyn = (size_t)Dp * (Dp + 1) / 2 * sizeof(double) + (size_t)Dp * Dp * sizeof(float);
-    static bool attr_set = false;  // the attribute belongs to the function
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)jacobi_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // set on every call (cheap next to the solve): the setting is per device
+    const hipError_t e = hipFuncSetAttribute((const void*)jacobi_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
     jacobi_kernel<<<dim3((unsigned)P), kJacobiThreads, dyn, st>>>(cov, D, U, lam);
     return hipGetLastError();
 }
