@@ -8,11 +8,13 @@
 // exact answer with ties already broken.
 //
 // Pipeline per call (one selection = one (pair, head)):
-//  1. threshold: exact k-th largest of a SAMPLE of scores (one run of 32
-//     consecutive blocks in every `stride` runs; in the fused path, the
-//     maximum of each lane's 32 or 16 tokens of those blocks).  Each sample
-//     value is a distinct token's score, so the k-th largest sample value is
-//     a lower bound of the true k-th largest: every true winner passes it.
+//  1. threshold: a lower bound of the k-th largest of a SAMPLE of scores
+//     (one run of 32 consecutive blocks in every `stride` runs; in the fused
+//     path, the maximum of each lane's 32 or 16 tokens of those blocks).
+//     Each sample value is a distinct token's score, so the k-th largest
+//     sample value -- and anything below it -- is a lower bound of the true
+//     k-th largest: every true winner passes it.  The bound used is the
+//     lower edge of the 22-bit key bin holding the sample's k-th largest.
 //  2. filter:    one pass over all scores appends key >= threshold to a
 //                candidate list (wavefront-aggregated atomics).
 //  3. select:    exact k largest composites of the candidates (radix select
@@ -205,9 +207,16 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __r
         if (threadIdx.x == 0) tau[m] = 0u;
         return;
     }
+    // Any lower bound of the k-th largest score is a valid threshold: two
+    // 11-bit radix levels locate the bin (the top 22 bits of the key) that
+    // holds the sample's k-th largest, and its lower edge is used -- within
+    // 2^-14 of that value, and every element of the bin is at or above it.
     DenseSrc src{scores + m * npad, n, stride, count};
-    const uint64_t T = kth_largest(src, k, sh);
-    if (threadIdx.x == 0) tau[m] = (uint32_t)(T >> 32);
+    uint64_t prefix = 0, pmask = 0;
+    int need = k;
+    radix_level(src, 53, 0x7FFu, prefix, pmask, need, sh);
+    radix_level(src, 42, 0x7FFu, prefix, pmask, need, sh);
+    if (threadIdx.x == 0) tau[m] = (uint32_t)(prefix >> 32);
 }
 
 // Candidates of one (selection, 4096-token chunk).  blockIdx.x is the
