@@ -42,6 +42,8 @@ def _np_keys(case):
         return g.standard_normal((1000, 64)).astype(np.float32), "f32"
     if case == "d96":
         return g.standard_normal((777, 96)).astype(np.float32), "f32"
+    if case == "d100_bf16":  # D not a multiple of 8: the pack's one-element staging path
+        return wl.to_bf16_exact(g.standard_normal((333, 100)).astype(np.float32) * 3), "bf16"
     if case == "boundaries":
         x = g.standard_normal((64 * 6, 128)).astype(np.float32)
         sc = np.abs(x).reshape(6, 64, 128).max(1).astype(np.float16).astype(np.float32)
@@ -58,7 +60,7 @@ def _np_keys(case):
     raise KeyError(case)
 
 
-PACK_CASES = ["tiny_f32", "ragged_bf16", "n1", "n63", "n65_bf16", "d64", "d96", "boundaries"]
+PACK_CASES = ["tiny_f32", "ragged_bf16", "n1", "n63", "n65_bf16", "d64", "d96", "d100_bf16", "boundaries"]
 
 
 @pytest.mark.parametrize("case", PACK_CASES)
@@ -273,6 +275,7 @@ FUSED_CASES = [  # (workload-ish, n, D, G, budget, k, mode)
     ("rand", 700, 128, 4, 48, 512, 0), ("rand", 5000, 64, 8, 92, 256, 0),
     ("rand", 20000, 128, 4, 0, 300, 0),      # every score 0: ties overflow -> repair path
     ("rand", 9000, 128, 2, 32, 1, 1), ("rand", 100, 128, 4, 2, 100, 2), ("rand", 1, 128, 4, 48, 1, 0),
+    ("rand", 3000, 100, 4, 40, 128, 0),   # D not a multiple of 8
 ]
 
 
