@@ -36,7 +36,7 @@ constexpr int kBuf = 4096;
 
 struct SelShared {
     uint32_t hist[kBins];
-    uint64_t buf[kBuf];
+    uint64_t buf[kBuf + 8];  // + 8 zero pads after the winners for the linear rank loop
     uint32_t wsum[kSelThreads / kWave];
     uint32_t nbuf;
     uint32_t bin, above, inbin;
@@ -126,6 +126,64 @@ __device__ uint32_t radix_level(const Src& src, int sft, uint32_t wm, uint64_t& 
     pmask |= (uint64_t)wm << sft;
     __syncthreads();
     return inbin;
+}
+
+__device__ __forceinline__ uint32_t shfl_xor_any(uint32_t v, int m)
+{
+    return (uint32_t)__shfl_xor((int)v, m, kWave);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_any(uint64_t v, int m)
+{
+    const uint32_t lo = shfl_xor_any((uint32_t)v, m), hi = shfl_xor_any((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one value per lane across the wavefront, descending by
+// lane: in every merge step the lane of each exchanged pair that lies in a
+// descending run of the current size keeps the larger value at the lower
+// lane (the last run spans the wavefront, so the result is descending).
+template <class T>
+__device__ __forceinline__ T wave_sort_desc(T v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+        for (int st = size >> 1; st > 0; st >>= 1) {
+            const T o = shfl_xor_any(v, st);
+            const bool keep_max = ((lane & size) == 0) == ((lane & st) == 0);
+            const T hi = v > o ? v : o, lo = v > o ? o : v;
+            v = keep_max ? hi : lo;
+        }
+    }
+    return v;
+}
+
+// Number of entries above x in nch chunks of 64, each sorted descending:
+// per chunk, binary lifting over the first 63 positions then one read of the
+// position reached (which exceeds x only when all 64 do).  Eight chunks'
+// searches run interleaved.
+template <class T>
+__device__ __forceinline__ int count_above(const T* a, int nch, T x)
+{
+    int r = 0;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+        int base[8], pos[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            base[q] = (c0 + q < nch ? c0 + q : nch - 1) * kWave;
+            pos[q] = 0;
+        }
+#pragma unroll
+        for (int st = kWave / 2; st > 0; st >>= 1)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) pos[q] += a[base[q] + pos[q] + st - 1] > x ? st : 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (c0 + q < nch) r += pos[q] + (a[base[q] + pos[q]] > x ? 1 : 0);
+    }
+    return r;
 }
 
 struct LdsSrc {
@@ -291,21 +349,68 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
     __syncthreads();
-    // rank of each winner by composite (its output position) and by token
-    // index (its position in the index-sorted list the union merges);
-    // index i < index j exactly when ~i > ~j in the low word
-    for (int i = threadIdx.x; i < k; i += blockDim.x) {
-        const uint64_t v = sh.buf[i];
-        const uint32_t lo = (uint32_t)v;
-        int r = 0, ri = 0;
-        for (int j = 0; j < k; ++j) {
-            const uint64_t u = sh.buf[j];
-            r += u > v ? 1 : 0;
-            ri += (uint32_t)u > lo ? 1 : 0;
+    // Place each winner by its rank among the k by composite (its output
+    // position) and by token index (its position in the index-sorted list
+    // the union merges); index i < index j exactly when ~i > ~j in the low
+    // word.
+    if (k <= kBins) {
+        // Merge ranking: every wave sorts 64-winner chunks descending in
+        // registers (composites in place in buf, low words into hist, which
+        // the radix levels no longer need); a winner's rank is then the sum
+        // over all chunks of how many entries exceed it, a 7-read binary
+        // search per chunk.  Zero pads fill the last chunk: a composite's
+        // low word is ~index with index < 2^31, so every real composite and
+        // every real low word is nonzero and the pads count below them all.
+        const int nch = (k + kWave - 1) / kWave;
+        for (int i = k + (int)threadIdx.x; i < nch * kWave; i += blockDim.x) sh.buf[i] = 0;
+        __syncthreads();
+        const int lane = lane_id();
+        for (int c = (int)(threadIdx.x / kWave); c < nch; c += (int)(blockDim.x / kWave)) {
+            const uint64_t v = sh.buf[c * kWave + lane];
+            const uint64_t sv = wave_sort_desc(v);
+            const uint32_t sl = wave_sort_desc((uint32_t)v);
+            sh.buf[c * kWave + lane] = sv;
+            sh.hist[c * kWave + lane] = sl;
         }
-        topk_idx[m * k + r] = (int32_t)(~lo);
-        if (topk_val) topk_val[m * k + r] = key_score((uint32_t)(v >> 32));
-        sorted_idx[m * k + ri] = (int32_t)(~lo);
+        __syncthreads();
+        for (int t = threadIdx.x; t < 2 * nch * kWave; t += blockDim.x) {
+            const bool by_index = t >= nch * kWave;
+            const int slot = by_index ? t - nch * kWave : t;
+            // sorted slot (chunk c, position p) holds a winner iff p < k - c * 64
+            if (slot >= k) continue;
+            if (!by_index) {
+                const uint64_t v = sh.buf[slot];
+                const int r = count_above(sh.buf, nch, v);
+                topk_idx[m * k + r] = (int32_t)(~(uint32_t)v);
+                if (topk_val) topk_val[m * k + r] = key_score((uint32_t)(v >> 32));
+            } else {
+                const uint32_t lo = sh.hist[slot];
+                sorted_idx[m * k + count_above(sh.hist, nch, lo)] = (int32_t)(~lo);
+            }
+        }
+    } else {
+        // Linear ranking, eight LDS reads in flight per step; eight zero pads
+        // after the k winners rank below every composite and every index.
+        if (threadIdx.x < 8) sh.buf[k + threadIdx.x] = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < k; i += blockDim.x) {
+            const uint64_t v = sh.buf[i];
+            const uint32_t lo = (uint32_t)v;
+            int r = 0, ri = 0;
+            for (int j = 0; j < k; j += 8) {
+                uint64_t u[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) u[q] = sh.buf[j + q];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    r += u[q] > v ? 1 : 0;
+                    ri += (uint32_t)u[q] > lo ? 1 : 0;
+                }
+            }
+            topk_idx[m * k + r] = (int32_t)(~lo);
+            if (topk_val) topk_val[m * k + r] = key_score((uint32_t)(v >> 32));
+            sorted_idx[m * k + ri] = (int32_t)(~lo);
+        }
     }
 }
 
