@@ -35,12 +35,11 @@ constexpr int kBins = 2048;
 constexpr int kBuf = 4096;
 
 struct SelShared {
-    uint32_t hist[kBins];
-    uint64_t buf[kBuf + 8];  // + 8 zero pads after the winners for the linear rank loop
-    uint32_t wsum[kSelThreads / kWave];
+    uint32_t hist[2][kBins];  // level l counts into hist[l & 1] and clears the other
+    uint64_t buf[kBuf + 8];   // + 8 zero pads after the winners for the linear rank loop
+    uint64_t wlo[kSelThreads / kWave], whi[kSelThreads / kWave];
     uint32_t nbuf;
     uint32_t bin, above, inbin;
-    uint64_t result;
 };
 
 struct DenseSrc {
@@ -68,64 +67,285 @@ struct CandSrc {
     }
 };
 
-// Exclusive scan of one value per thread across the workgroup.
-__device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh)
+struct LdsSrc {
+    const uint64_t* c;
+    int64_t count;
+    __device__ __forceinline__ uint64_t get(int64_t e, bool& ok) const
+    {
+        ok = true;
+        return c[e];
+    }
+};
+
+// Radix select over 64-bit values x below 2^bits, most significant digit
+// first: 11-bit digits from bit `bits` down (the last one narrower).  The
+// digits fixed so far form `prefix` under the contiguous top mask `pmask`;
+// `need` is the rank (1 = largest) still sought among the values that match
+// them.  Once the bin of the sought value holds it alone, the k largest are
+// exactly the values whose masked x is at or above the prefix.  The values
+// are the composites themselves (bits = 64), or their offsets from the
+// smallest one (bits = the bit length of the range): then the first digit
+// already spreads them over all bins, where the top bits of a selection's
+// candidates are nearly all equal and their histogram would funnel every
+// add into a few bins.
+struct Radix {
+    uint64_t prefix, pmask;
+    int need, lvl, bits;
+    __device__ __forceinline__ int hi() const { return bits - 11 * lvl; }  // digit covers [shift, hi)
+    __device__ __forceinline__ int shift() const { return hi() > 11 ? hi() - 11 : 0; }
+    __device__ __forceinline__ uint32_t mask() const { return (1u << (hi() - shift())) - 1u; }
+    __device__ __forceinline__ bool done() const { return hi() <= 0; }
+    __device__ __forceinline__ bool in(uint64_t x) const { return (x & pmask) == prefix; }
+    __device__ __forceinline__ uint32_t digit(uint64_t x) const { return (uint32_t)(x >> shift()) & mask(); }
+    __device__ __forceinline__ bool at_or_above(uint64_t x) const { return (x & pmask) >= prefix; }
+};
+
+// Zeroes the first level's histogram (followed by a barrier).
+__device__ __forceinline__ Radix radix_start(int need, SelShared& sh)
 {
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    uint32_t x = v;
+    for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[0][i] = 0;
+    __syncthreads();
+    return Radix{0, 0, need, 0, 64};
+}
+
+// Values every thread of the workgroup reads alike (from LDS), moved to
+// scalar registers.
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
+{
+    return ((uint64_t)uniform_u32((uint32_t)(v >> 32)) << 32) | uniform_u32((uint32_t)v);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, kWave);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Radix over offsets from the smallest element, `lo` (lo_t, hi_t: this
+// thread's extremes; ~0 and 0 when it holds none).  Zeroes the first
+// histogram.
+__device__ Radix radix_start_range(int need, uint64_t lo_t, uint64_t hi_t, SelShared& sh,
+                                   uint64_t& lo)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint64_t a = shfl_xor_u64(lo_t, o), b = shfl_xor_u64(hi_t, o);
+        lo_t = a < lo_t ? a : lo_t;
+        hi_t = b > hi_t ? b : hi_t;
+    }
+    const int wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    if (lane_id() == 0) {
+        sh.wlo[wave] = lo_t;
+        sh.whi[wave] = hi_t;
+    }
+    for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[0][i] = 0;
+    __syncthreads();
+    uint64_t hi = 0;
+    lo = ~0ull;
+    for (int w = 0; w < nw; ++w) {
+        lo = sh.wlo[w] < lo ? sh.wlo[w] : lo;
+        hi = sh.whi[w] > hi ? sh.whi[w] : hi;
+    }
+    lo = uniform_u64(lo);
+    hi = uniform_u64(hi);
+    const int bits = hi > lo ? 64 - __clzll((long long)(hi - lo)) : 1;
+    return Radix{0, 0, need, 0, bits};
+}
+
+// Histogram of the current level; the next level's buffer is zeroed here
+// (its last reader, the previous level's bin search, ended at a barrier).
+__device__ __forceinline__ uint32_t* level_begin(const Radix& r, SelShared& sh)
+{
+    uint32_t* nxt = sh.hist[(r.lvl + 1) & 1];
+    for (int i = threadIdx.x; i < kBins; i += blockDim.x) nxt[i] = 0;
+    return sh.hist[r.lvl & 1];
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x)
+{
+    const int lane = lane_id();
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         const uint32_t y = __shfl_up(x, o, kWave);
         if (lane >= o) x += y;
     }
-    if (lane == kWave - 1) sh.wsum[wave] = x;
-    __syncthreads();
-    uint32_t off = 0;
-    for (int w = 0; w < wave; ++w) off += sh.wsum[w];
-    __syncthreads();
-    return off + x - v;
+    return x;
 }
 
-// One radix level: histogram of the 11-bit digit at `sft` over the elements
-// matching (prefix, pmask); picks the bin holding the need-th largest and
-// narrows prefix/pmask/need.  Returns the number of elements in that bin.
-template <class Src>
-__device__ uint32_t radix_level(const Src& src, int sft, uint32_t wm, uint64_t& prefix,
-                                uint64_t& pmask, int& need, SelShared& sh)
+// After the histogram: the first wavefront finds the bin holding the
+// need-th largest, then every thread fixes that digit.  Bins are taken top
+// first: lane l sums bins 2047 - 32l down to 2016 - 32l, a wavefront prefix
+// sum over those groups names the group that holds the sought element, and
+// a second prefix sum over that group's 32 bins (one per lane) names the
+// bin.  Returns the number of elements in the bin.
+__device__ uint32_t level_end(Radix& r, SelShared& sh)
 {
-    for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[i] = 0;
-    if (threadIdx.x == 0) {
-        sh.bin = 0;
-        sh.above = 0;
-        sh.inbin = 0;
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const uint32_t* h = sh.hist[r.lvl & 1];
+        const int lane = threadIdx.x;
+        const uint4* h4 = reinterpret_cast<const uint4*>(h + kBins - 32 * (lane + 1));
+        uint32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint4 x = h4[j];
+            sum += x.x + x.y + x.z + x.w;
+        }
+        const uint32_t need = (uint32_t)r.need;
+        uint32_t inc = wave_incl_sum(sum);
+        // the first group whose running total reaches need
+        const int g = __builtin_ctzll(__ballot(inc >= need));
+        const uint32_t before = (uint32_t)__shfl((int)(inc - sum), g, kWave);
+        const int b = kBins - 1 - 32 * g - (lane & 31);  // lanes 32..63 repeat 0..31
+        const uint32_t c = h[b];
+        inc = before + wave_incl_sum(lane < 32 ? c : 0u);
+        const int l = __builtin_ctzll(__ballot(lane < 32 && inc >= need));
+        if (lane == l) {
+            sh.bin = (uint32_t)b;
+            sh.above = inc - c;
+            sh.inbin = c;
+        }
     }
+    __syncthreads();
+    const int sft = r.shift();
+    r.need -= (int)uniform_u32(sh.above);
+    r.prefix |= (uint64_t)uniform_u32(sh.bin) << sft;
+    r.pmask |= (uint64_t)r.mask() << sft;
+    ++r.lvl;
+    return uniform_u32(sh.inbin);  // read before the next level's first barrier
+}
+
+// One radix level over src, four elements per thread loaded before any is
+// counted.
+template <class Src>
+__device__ uint32_t radix_level(const Src& src, Radix& r, SelShared& sh)
+{
+    uint32_t* h = level_begin(r, sh);
+    const int64_t bd = blockDim.x;
+    for (int64_t e0 = threadIdx.x; e0 < src.count; e0 += 4 * bd) {
+        uint64_t v[4];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t e = e0 + u * bd;
+            ok[u] = false;
+            v[u] = e < src.count ? src.get(e, ok[u]) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (ok[u] && r.in(v[u])) atomicAdd(&h[r.digit(v[u])], 1u);
+    }
+    return level_end(r, sh);
+}
+
+// Radix levels over src until the sought element's bin fits in LDS; that
+// bin is then copied to sh.buf and the remaining levels run there.
+template <class Src>
+__device__ Radix kth_largest(const Src& src, int need, SelShared& sh)
+{
+    Radix r = radix_start(need, sh);
+    uint32_t inbin;
+    do {
+        inbin = radix_level(src, r, sh);
+    } while (inbin > (uint32_t)kBuf && !r.done());
+    if (inbin <= 1) return r;
+    if (threadIdx.x == 0) sh.nbuf = 0;
     __syncthreads();
     for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
         bool ok;
         const uint64_t v = src.get(e, ok);
-        if (ok && (v & pmask) == prefix) atomicAdd(&sh.hist[(uint32_t)(v >> sft) & wm], 1u);
+        if (ok && r.in(v)) {
+            const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
+            if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+        }
     }
     __syncthreads();
-    // reversed bins 2t, 2t+1 -> bins 2047-2t, 2046-2t (top first)
-    const int t = threadIdx.x;
-    const uint32_t c0 = sh.hist[kBins - 1 - 2 * t], c1 = sh.hist[kBins - 2 - 2 * t];
-    const uint32_t ex = block_excl_scan(c0 + c1, sh);
-    if (ex < (uint32_t)need && (uint32_t)need <= ex + c0) {
-        sh.bin = kBins - 1 - 2 * t;
-        sh.above = ex;
-        sh.inbin = c0;
-    } else if (ex + c0 < (uint32_t)need && (uint32_t)need <= ex + c0 + c1) {
-        sh.bin = kBins - 2 - 2 * t;
-        sh.above = ex + c0;
-        sh.inbin = c1;
+    const LdsSrc lsrc{sh.buf, (int64_t)inbin};
+    while (!r.done() && inbin > 1) inbin = radix_level(lsrc, r, sh);
+    return r;
+}
+
+// Up to kRegSlots candidates per thread held in registers: slot q of
+// thread t is candidate q * blockDim + t.
+constexpr int kRegSlots = 16;
+
+struct RegCands {
+    uint64_t v[kRegSlots];
+    uint32_t valid;  // bit q: slot q holds a candidate
+};
+
+__device__ __forceinline__ void load_regs(const uint64_t* c, int64_t cnt, RegCands& rc)
+{
+    rc.valid = 0;
+#pragma unroll
+    for (int q = 0; q < kRegSlots; ++q) {
+        const int64_t e = (int64_t)q * blockDim.x + threadIdx.x;
+        const bool ok = e < cnt;
+        rc.v[q] = ok ? c[e] : 0;
+        rc.valid |= ok ? 1u << q : 0u;
     }
-    __syncthreads();
-    const uint32_t bin = sh.bin, inbin = sh.inbin;
-    need -= (int)sh.above;
-    prefix |= (uint64_t)bin << sft;
-    pmask |= (uint64_t)wm << sft;
-    __syncthreads();
-    return inbin;
+}
+
+// Radix levels over the candidates in registers, which are replaced by
+// their offsets from the smallest one (returned in `base`).
+__device__ Radix kth_largest_regs(RegCands& rc, int need, SelShared& sh, uint64_t& base)
+{
+    uint64_t lo = ~0ull, hi = 0;
+#pragma unroll
+    for (int q = 0; q < kRegSlots; ++q)
+        if ((rc.valid >> q) & 1u) {
+            lo = rc.v[q] < lo ? rc.v[q] : lo;
+            hi = rc.v[q] > hi ? rc.v[q] : hi;
+        }
+    Radix r = radix_start_range(need, lo, hi, sh, base);
+#pragma unroll
+    for (int q = 0; q < kRegSlots; ++q) {
+        rc.v[q] -= base;
+        // opaque to the optimiser: otherwise the winners' offset + base
+        // folds back to the original value, which then stays live too
+        asm volatile("" : "+v"(rc.v[q]));
+    }
+    for (;;) {
+        uint32_t* h = level_begin(r, sh);
+#pragma unroll
+        for (int q = 0; q < kRegSlots; ++q)
+            if (((rc.valid >> q) & 1u) && r.in(rc.v[q])) atomicAdd(&h[r.digit(rc.v[q])], 1u);
+        if (level_end(r, sh) <= 1 || r.done()) break;
+    }
+    return r;
+}
+
+// Appends the candidates at or above the cut to sh.buf with one LDS atomic
+// per wavefront: the wavefront's winners are counted first, then each is
+// placed at the wavefront's base plus the winners before it (earlier slots,
+// then lower lanes of its own slot).
+__device__ __forceinline__ void winners_from_regs(const RegCands& rc, const Radix& r, uint64_t base,
+                                                  SelShared& sh)
+{
+    const int lane = lane_id();
+    uint32_t wins = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < kRegSlots; ++q) {
+        const bool win = ((rc.valid >> q) & 1u) && r.at_or_above(rc.v[q]);
+        wins |= win ? 1u << q : 0u;
+        total += (uint32_t)__popcll(__ballot(win));
+    }
+    uint32_t slot = 0;
+    if (lane == 0 && total != 0) slot = atomicAdd(&sh.nbuf, total);
+    slot = (uint32_t)__shfl((int)slot, 0, kWave);
+#pragma unroll
+    for (int q = 0; q < kRegSlots; ++q) {
+        const bool win = (wins >> q) & 1u;
+        const uint64_t b = __ballot(win);
+        if (win) sh.buf[slot + (uint32_t)__popcll(b & lanes_below(lane))] = rc.v[q] + base;
+        slot += (uint32_t)__popcll(b);
+    }
 }
 
 __device__ __forceinline__ uint32_t shfl_xor_any(uint32_t v, int m)
@@ -186,56 +406,6 @@ __device__ __forceinline__ int count_above(const T* a, int nch, T x)
     return r;
 }
 
-struct LdsSrc {
-    const uint64_t* c;
-    int64_t count;
-    __device__ __forceinline__ uint64_t get(int64_t e, bool& ok) const
-    {
-        ok = true;
-        return c[e];
-    }
-};
-
-// Exact need-th largest (1-based) of the unique composites of src: 11-bit
-// radix levels over src until the bin that holds it fits in LDS, then the
-// remaining levels over that LDS copy.
-template <class Src>
-__device__ uint64_t kth_largest(const Src& src, int need, SelShared& sh)
-{
-    uint64_t prefix = 0, pmask = 0;
-    const int shifts[6] = {53, 42, 31, 20, 9, 0};
-    int lvl = 0;
-    uint32_t inbin = 0;
-    for (; lvl < 6; ++lvl) {
-        inbin = radix_level(src, shifts[lvl], lvl == 5 ? 0x1FFu : 0x7FFu, prefix, pmask, need, sh);
-        if (inbin <= (uint32_t)kBuf) break;
-    }
-    // gather the bin into LDS
-    if (threadIdx.x == 0) sh.nbuf = 0;
-    __syncthreads();
-    for (int64_t e = threadIdx.x; e < src.count; e += blockDim.x) {
-        bool ok;
-        const uint64_t v = src.get(e, ok);
-        if (ok && (v & pmask) == prefix) {
-            const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
-            if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
-        }
-    }
-    __syncthreads();
-    const LdsSrc lsrc{sh.buf, (int64_t)(inbin < (uint32_t)kBuf ? inbin : kBuf)};
-    for (++lvl; lvl < 6 && inbin > 1; ++lvl)
-        inbin = radix_level(lsrc, shifts[lvl], lvl == 5 ? 0x1FFu : 0x7FFu, prefix, pmask, need, sh);
-    // the single element with this prefix
-    if (threadIdx.x == 0) sh.result = 0;
-    __syncthreads();
-    for (int64_t e = threadIdx.x; e < lsrc.count; e += blockDim.x)
-        if ((sh.buf[e] & pmask) == prefix) sh.result = sh.buf[e];
-    __syncthreads();
-    const uint64_t T = sh.result;
-    __syncthreads();
-    return T;
-}
-
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt, uint32_t v)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -270,11 +440,10 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __r
     // holds the sample's k-th largest, and its lower edge is used -- within
     // 2^-14 of that value, and every element of the bin is at or above it.
     DenseSrc src{scores + m * npad, n, stride, count};
-    uint64_t prefix = 0, pmask = 0;
-    int need = k;
-    radix_level(src, 53, 0x7FFu, prefix, pmask, need, sh);
-    radix_level(src, 42, 0x7FFu, prefix, pmask, need, sh);
-    if (threadIdx.x == 0) tau[m] = (uint32_t)(prefix >> 32);
+    Radix r = radix_start(k, sh);
+    radix_level(src, r, sh);
+    radix_level(src, r, sh);
+    if (threadIdx.x == 0) tau[m] = (uint32_t)(r.prefix >> 32);
 }
 
 // Candidates of one (selection, 4096-token chunk).  blockIdx.x is the
@@ -322,7 +491,8 @@ __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ s
     }
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+// Eight waves per SIMD: two workgroups per CU.
+__global__ __launch_bounds__(kSelThreads, 8) void select_kernel(
     const float* __restrict__ scores, int64_t n, int64_t npad, const uint32_t* __restrict__ counts,
     const uint64_t* __restrict__ cand, int64_t cap, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_val, int32_t* __restrict__ sorted_idx)
@@ -330,22 +500,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ SelShared sh;
     const int64_t m = blockIdx.x;
     const int64_t cnt = counts[m];
-    uint64_t T;
     const bool dense = cnt > cap;
-    DenseSrc dsrc{scores + m * npad, n, 1, npad};
-    CandSrc csrc{cand + m * cap, cnt};
-    T = dense ? kth_largest(dsrc, k, sh) : kth_largest(csrc, k, sh);
-    // gather the k winners (composites >= T); each one's rank among them is
-    // its output position (composites are unique)
-    if (threadIdx.x == 0) sh.nbuf = 0;
-    __syncthreads();
-    const int64_t total = dense ? dsrc.count : csrc.count;
-    for (int64_t e = threadIdx.x; e < total; e += blockDim.x) {
-        bool ok;
-        const uint64_t v = dense ? dsrc.get(e, ok) : csrc.get(e, ok);
-        if (ok && v >= T) {
-            const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
-            if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+    if (!dense && cnt <= (int64_t)kRegSlots * blockDim.x) {
+        // candidates read once into registers; the radix levels and the
+        // winner gather run from there
+        RegCands rc;
+        uint64_t base;
+        load_regs(cand + m * cap, cnt, rc);
+        const Radix r = kth_largest_regs(rc, k, sh, base);
+        if (threadIdx.x == 0) sh.nbuf = 0;
+        __syncthreads();
+        winners_from_regs(rc, r, base, sh);
+    } else {
+        DenseSrc dsrc{scores + m * npad, n, 1, npad};
+        CandSrc csrc{cand + m * cap, cnt};
+        const Radix r = dense ? kth_largest(dsrc, k, sh) : kth_largest(csrc, k, sh);
+        if (threadIdx.x == 0) sh.nbuf = 0;
+        __syncthreads();
+        const int64_t total = dense ? dsrc.count : csrc.count;
+        for (int64_t e = threadIdx.x; e < total; e += blockDim.x) {
+            bool ok;
+            const uint64_t v = dense ? dsrc.get(e, ok) : csrc.get(e, ok);
+            if (ok && r.at_or_above(v)) {
+                const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
+                if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+            }
         }
     }
     __syncthreads();
@@ -370,7 +549,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const uint64_t sv = wave_sort_desc(v);
             const uint32_t sl = wave_sort_desc((uint32_t)v);
             sh.buf[c * kWave + lane] = sv;
-            sh.hist[c * kWave + lane] = sl;
+            sh.hist[0][c * kWave + lane] = sl;
         }
         __syncthreads();
         for (int t = threadIdx.x; t < 2 * nch * kWave; t += blockDim.x) {
@@ -384,8 +563,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 topk_idx[m * k + r] = (int32_t)(~(uint32_t)v);
                 if (topk_val) topk_val[m * k + r] = key_score((uint32_t)(v >> 32));
             } else {
-                const uint32_t lo = sh.hist[slot];
-                sorted_idx[m * k + count_above(sh.hist, nch, lo)] = (int32_t)(~lo);
+                const uint32_t lo = sh.hist[0][slot];
+                sorted_idx[m * k + count_above(sh.hist[0], nch, lo)] = (int32_t)(~lo);
             }
         }
     } else {
