@@ -131,8 +131,9 @@ struct ScanArgs {
     uint32_t* counts;      // FILTER: [P][G]
     uint64_t* cand;        // FILTER: [P][G][cap]
     int64_t cap;
-    const uint32_t* only;  // optional [P] flags: pairs whose flag is 0 are skipped
+    const uint32_t* list;  // optional (score mode): list[0] pairs listed in list[1..]; only they are scanned
 };
+constexpr int kListRows = 4;  // workgroup rows that walk a pair list
 // mode: 0 store scores, 1 filter into candidates, 2 per-lane maxima
 hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream_t st);
 
@@ -153,7 +154,7 @@ struct TopkLayout {
     int64_t cap;         // candidate capacity per selection
     bool lanemax;        // fused threshold from per-lane maxima of the sample
     size_t off_tau, off_count, off_cand, off_sorted, bytes;  // top-k from given scores
-    size_t off_flags, off_sample, off_repair, bytes_fused;  // fused scan + top-k
+    size_t off_list, off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };
 TopkLayout topk_layout(int P, int G, int64_t n, int k);
 hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,

@@ -146,8 +146,9 @@ struct ChanWords {
 
 enum { kStore = 0, kFilter = 1, kLaneMax = 2 };
 
+// One workgroup's tile of pair p.
 template <int G, int TOK, int MODE>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
+__device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p)
 {
     constexpr int kParts = 64 / TOK;       // lanes per block
     constexpr int kBlocksPerWave = TOK;    // 64 / kParts
@@ -158,8 +159,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     __shared__ __attribute__((aligned(16))) float s_stage[FILTER ? kScanThreads / kWave : 1][kWave][TOK + 4];
     __shared__ uint32_t s_wcount[kScanThreads / kWave][G];
 
-    const int p = blockIdx.y;
-    if (a.only && a.only[p] == 0) return;
     const int A = a.n_active[p];
     for (int e = threadIdx.x; e < A; e += kScanThreads) {
         const int j = a.active[(size_t)p * a.D + e];
@@ -311,12 +310,30 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
     }
 }
 
+// blockIdx.y is the pair; with a pair list (score mode only), the rows of
+// the grid take the listed pairs in turn instead.
+template <int G, int TOK, int MODE>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a)
+{
+    if (MODE == kStore && a.list) {
+        const uint32_t nlist = a.list[0];
+        for (uint32_t r = blockIdx.y; r < nlist; r += gridDim.y) {
+            scan_pair<G, TOK, MODE>(a, (int)a.list[1 + r]);
+            __syncthreads();  // the pair's LDS tables are rewritten by the next one
+        }
+        return;
+    }
+    scan_pair<G, TOK, MODE>(a, (int)blockIdx.y);
+}
+
 template <int G, int MODE>
 hipError_t launch_g(const ScanArgs& a, int P, hipStream_t st)
 {
     constexpr int TOK = G <= 4 ? 32 : 16;
     constexpr int per_wg = (kScanThreads / kWave) * TOK;  // blocks per workgroup
-    dim3 grid((unsigned)((a.nlb + per_wg - 1) / per_wg), (unsigned)P);
+    // a pair list is walked by kListRows rows of workgroups
+    const int rows = a.list ? (P < kListRows ? P : kListRows) : P;
+    dim3 grid((unsigned)((a.nlb + per_wg - 1) / per_wg), (unsigned)rows);
     scan_kernel<G, TOK, MODE><<<grid, kScanThreads, 0, st>>>(a);
     return hipGetLastError();
 }

@@ -412,15 +412,33 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt,
     if (i < cnt) p[i] = v;
 }
 
-// flags[p] = 1 when some head of pair p collected more candidates than fit.
-__global__ __launch_bounds__(256) void overflow_kernel(const uint32_t* __restrict__ counts, int P,
-                                                       int G, int64_t cap, uint32_t* __restrict__ flags)
+// The pairs with some head whose candidates overflowed their capacity, in
+// pair order: list[0] = how many, list[1..] = the pairs.  One workgroup.
+__global__ __launch_bounds__(kSelThreads) void overflow_list_kernel(const uint32_t* __restrict__ counts,
+                                                                   int P, int G, int64_t cap,
+                                                                   uint32_t* __restrict__ list)
 {
-    const int p = blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= P) return;
-    uint32_t f = 0;
-    for (int h = 0; h < G; ++h) f |= (int64_t)counts[(size_t)p * G + h] > cap ? 1u : 0u;
-    flags[p] = f;
+    __shared__ uint32_t wsum[kSelThreads / kWave];
+    const int lane = lane_id(), wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    uint32_t base = 0;
+    for (int p0 = 0; p0 < P; p0 += blockDim.x) {
+        const int p = p0 + (int)threadIdx.x;
+        bool f = false;
+        if (p < P)
+            for (int h = 0; h < G; ++h) f |= (int64_t)counts[(size_t)p * G + h] > cap;
+        const uint64_t b = __ballot(f);
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(b);
+        __syncthreads();
+        uint32_t off = base, all = 0;
+        for (int w = 0; w < nw; ++w) {
+            off += w < wave ? wsum[w] : 0u;
+            all += wsum[w];
+        }
+        if (f) list[1 + off + (uint32_t)__popcll(b & lanes_below(lane))] = (uint32_t)p;
+        base += all;
+        __syncthreads();  // wsum is rewritten by the next round
+    }
+    if (threadIdx.x == 0) list[0] = base;
 }
 
 __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __restrict__ scores,
@@ -612,27 +630,34 @@ __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __res
     __syncthreads();
     int32_t val[kPer];
     int pos[kPer];
+    // binary lifting over each other list, steps from the largest power of
+    // two not above k; the G - 1 searches of an element run interleaved
+    const int top = 1 << (31 - __clz(k));
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-        const int e = threadIdx.x + u * (int)blockDim.x;
         pos[u] = -1;
         val[u] = 0;
+        if (u * (int)blockDim.x >= total) continue;
+        const int e = threadIdx.x + u * (int)blockDim.x;
         if (e < total) {
             const int h = e / k;
             const int32_t x = a[e];
-            int r = e - h * k;
-            for (int h2 = 0; h2 < G; ++h2) {
-                if (h2 == h) continue;
-                const int32_t* l = a + h2 * k;
-                int lo = 0, hi = k;  // first element of list h2 placed after x
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    const bool before = h2 < h ? l[mid] <= x : l[mid] < x;
-                    if (before) lo = mid + 1;
-                    else hi = mid;
+            int cnt[kMaxG];
+#pragma unroll
+            for (int h2 = 0; h2 < kMaxG; ++h2) cnt[h2] = 0;
+            for (int st = top; st > 0; st >>= 1) {
+#pragma unroll
+                for (int h2 = 0; h2 < kMaxG; ++h2) {
+                    const int np = cnt[h2] + st;
+                    if (h2 < G && h2 != h && np <= k) {
+                        const int32_t y = a[h2 * k + np - 1];
+                        if (h2 < h ? y <= x : y < x) cnt[h2] = np;
+                    }
                 }
-                r += lo;
             }
+            int r = e - h * k;
+#pragma unroll
+            for (int h2 = 0; h2 < kMaxG; ++h2) r += (h2 < G && h2 != h) ? cnt[h2] : 0;
             val[u] = x;
             pos[u] = r;
         }
@@ -694,8 +719,8 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k)
     L.off_cand = up(L.off_count + (size_t)L.m * 4);
     L.off_sorted = up(L.off_cand + (size_t)L.m * (size_t)L.cap * 8);
     L.bytes = L.off_sorted + (size_t)L.m * (size_t)k * 4;
-    L.off_flags = up(L.bytes);
-    L.off_sample = up(L.off_flags + (size_t)P * 4);
+    L.off_list = up(L.bytes);
+    L.off_sample = up(L.off_list + ((size_t)P + 1) * 4);
     L.off_repair = up(L.off_sample + (size_t)L.m * (size_t)L.sample_nlb * 64 * 4);
     L.bytes_fused = L.off_repair + (size_t)L.m * (size_t)nb * 64 * 4;
     return L;
@@ -745,7 +770,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
     uint32_t* tau = (uint32_t*)(w + L.off_tau);
     uint32_t* counts = (uint32_t*)(w + L.off_count);
     uint64_t* cand = (uint64_t*)(w + L.off_cand);
-    uint32_t* flags = (uint32_t*)(w + L.off_flags);
+    uint32_t* list = (uint32_t*)(w + L.off_list);
     float* sample = (float*)(w + L.off_sample);
     float* repair = (float*)(w + L.off_repair);
     hipError_t e;
@@ -757,7 +782,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         a.stride = L.stride;
         a.nlb = L.sample_nlb;
         a.out = sample;
-        a.only = nullptr;
+        a.list = nullptr;
         if ((e = launch_scan_args(a, P, G, L.lanemax ? 2 : 0, st)) != hipSuccess) return e;
         // every lane maximum is a distinct token's score, so the k-th largest
         // of them is still a lower bound of the k-th largest score
@@ -774,17 +799,17 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         a.counts = counts;
         a.cand = cand;
         a.cap = L.cap;
-        a.only = nullptr;
+        a.list = nullptr;
         if ((e = launch_scan_args(a, P, G, 1, st)) != hipSuccess) return e;
     }
     if (stages & 4) {
         // pairs whose candidates overflowed get their full scores recomputed
-        overflow_kernel<<<dim3((unsigned)((P + 255) / 256)), 256, 0, st>>>(counts, P, G, L.cap, flags);
+        overflow_list_kernel<<<dim3(1), kSelThreads, 0, st>>>(counts, P, G, L.cap, list);
         a = base;
         a.stride = 1;
         a.nlb = nb;
         a.out = repair;
-        a.only = flags;
+        a.list = list;
         if ((e = launch_scan_args(a, P, G, 0, st)) != hipSuccess) return e;
         // exact top-k of the candidates (or of the repaired scores), union
         int32_t* sorted = (int32_t*)(w + L.off_sorted);
