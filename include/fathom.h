@@ -153,12 +153,22 @@ int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P
  *   nb_cap               blocks per index row: 0 for a dense index (nb),
  *                        else the capacity it was allocated with (>= nb)
  *   depth, active, n_active, q_used   a plan from fathom_plan
- *   scores [P][G][npad]  float32 output.  Score of token i for head h:
- *       s = 0; for each active channel j in ascending order:
- *           s = fma(q_used[h][j], khat_ij, s)
- *       where khat_ij = (2 c_t + 1 - 2^t) * 2^-t * scale is the exact
- *       dequantised t_j-plane prefix c_t = c >> (4 - t_j).  Padding tokens
- *       are -inf.
+ *   scores [P][G][npad]  float32 output: the dot product of q_used[h]
+ *       with the dequantised prefix keys, khat_ij = (2 c_t + 1 - 2^t) *
+ *       2^-t * scale (c_t = c >> (4 - t_j)), evaluated exactly and rounded
+ *       once.  Fixed-point contract, per head h and 64-token block b:
+ *         sigma_h = 31 - floor(log2 max_j |q_used[h][j]|) over the read
+ *                   channels (0 if all are 0);
+ *         E_b     = f_b - 15, f_b the largest binary16 exponent field of the
+ *                   read channels' scales in the block (at least 1);
+ *         A_hjb   = trunc(fl32(fl32(q_used[h][j] 2^sigma_h) * scale_jb) *
+ *                   2^-(E_b + 3)), an integer with |A| <= 2^30;
+ *         S_i     = sum_j A_hjb (2 c'_ij + 2^(4-t_j) - 16), c' = c_t 2^(4-t_j),
+ *                   an exact integer;
+ *         score   = fl32(S_i 2^(E_b - 1 - sigma_h)), round to nearest even.
+ *       The result differs from the real dot product by at most
+ *       15 (#read channels) 2^(E_b - 1 - sigma_h) + 2^-24 sum_j |q k| before
+ *       the final rounding.  Padding tokens are -inf.
  * Errors: ERR_ARG (null), ERR_SHAPE, ERR_ALIGN.
  */
 int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
@@ -191,15 +201,16 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
  *
  * Same inputs as fathom_scan plus k, and the outputs of fathom_topk, which
  * are identical to fathom_scan + fathom_topk on the same inputs.  Internally:
- * the scores of every s-th block (s ~ sqrt(n / 4k), a power of two) are
- * computed first and the exact k-th largest of that sample is taken as each
- * head's threshold -- a lower bound of the true k-th largest, since the
- * sample is a subset -- then one pass over the whole index keeps only the
- * scores at or above it as candidates, and the k best candidates are
- * selected exactly.  A head whose candidates exceed their capacity (possible
- * only with massively tied scores) has its pair rescanned into a full score
- * buffer inside the workspace and is selected from there; results are exact
- * either way.
+ * the scores of one run of 32 blocks in every s runs (s ~ sqrt(n / 4k), a
+ * power of two) are computed first -- as maxima of groups of 16 tokens once
+ * the sample is large -- and the ceil(2k / s)-th largest sample value is
+ * taken as each head's threshold (with s = 1: the exact k-th largest); one
+ * pass over the whole index then keeps the scores at or above it as
+ * candidates, and the k best candidates are selected exactly.  A head that
+ * ends up with fewer than k candidates (the sample misjudged it) or more
+ * than their capacity (massive ties) has its pair rescanned into a full
+ * score buffer inside the workspace and is selected from there; results are
+ * exact either way.
  *   ws  device workspace of at least fathom_scan_topk_workspace_bytes(); it
  *       includes that fallback buffer (P * G * npad floats), which is only
  *       written when a capacity is exceeded.

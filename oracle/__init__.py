@@ -5,9 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 (``sparse_attention_key_amd``) never imports it, and it imports nothing from
 the product.  It holds two independent descriptions of the method:
 
-* ``fathom_oracle.c`` (loaded through ctypes): the plain fp32/exact-integer
-  procedure -- pack, plan, fp32 score contract, top-k, union -- one
-  (layer, KV head) pair per call;
+* ``fathom_oracle.c`` (loaded through ctypes): the plain procedure -- pack,
+  plan, the fixed-point score contract (exact integer sums per block, one
+  final rounding), top-k, union -- one (layer, KV head) pair per call;
 * ``ref64`` (numpy, float64): the real-valued definitions used for the
   tolerance checks (dequantised prefix keys and the exact score sum).
 
@@ -77,8 +77,8 @@ def lib():
         L.orc_water_level.restype = ctypes.c_float
         L.orc_plan.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
         L.orc_plan.restype = ctypes.c_float
-        L.orc_scores_f32.argtypes = [P, P, i64, i32, P, P, i32, P]
-        L.orc_scores_f32.restype = None
+        L.orc_scores.argtypes = [P, P, i64, i32, P, P, i32, P]
+        L.orc_scores.restype = None
         L.orc_scores_f64.argtypes = [P, P, i64, i32, P, P, i32, P]
         L.orc_scores_f64.restype = None
         L.orc_topk.argtypes = [P, i64, i32, P, P]
@@ -166,7 +166,9 @@ def plan(q, sigma2, budget: int, mode: int = PLAN_WATERFILL, rot=None):
     return depth, float(theta), q_used
 
 
-def scores_f32(planes, scales, n: int, depth, q_used):
+def scores(planes, scales, n: int, depth, q_used):
+    """Scores under the fixed-point contract (exact integer sum per block,
+    one final rounding to float32); tokens >= n are -inf."""
     planes = _c(planes, np.uint64)
     scales = _c(scales, np.uint16)
     depth = _c(depth, np.uint8)
@@ -174,7 +176,7 @@ def scores_f32(planes, scales, n: int, depth, q_used):
     G, D = q_used.shape
     nb = (n + 63) // 64
     out = np.zeros((G, nb * 64), np.float32)
-    lib().orc_scores_f32(_p(planes), _p(scales), n, D, _p(depth), _p(q_used), G, _p(out))
+    lib().orc_scores(_p(planes), _p(scales), n, D, _p(depth), _p(q_used), G, _p(out))
     return out
 
 
@@ -207,7 +209,7 @@ def union(idx_gk):
 
 
 def step(planes, scales, n, q, sigma2, budget, k, mode=PLAN_WATERFILL, rot=None):
-    """plan + f32 scores + per-head top-k + union for one pair."""
+    """plan + scores + per-head top-k + union for one pair."""
     planes = _c(planes, np.uint64)
     scales = _c(scales, np.uint16)
     q = _c(q, np.float32)

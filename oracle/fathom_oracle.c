@@ -286,34 +286,75 @@ float orc_plan(const float* q, const float* sigma2, const float* rot, int G, int
 
 /* ------------------------------------------------------------------- scan */
 
-/* Approximate scores, fp32 contract: for each token i and head h,
- *   s = 0; for every channel j with t_j > 0, ascending: s = fma(q_hj, k_ij, s)
- * where k_ij is the exact dequantised t_j-plane prefix.  This is the plain
- * fp32 dot product of the query with the prefix-decoded key ("G multiply-adds
- * per extracted element", limitations section), fixed to ascending channel
- * order so that every implementation rounds identically. */
-void orc_scores_f32(const uint64_t* planes, const uint16_t* scales, int64_t n, int D,
-                    const uint8_t* depth, const float* q_used, int G, float* scores)
+/* Approximate scores, fixed-point contract.  The real value is the same dot
+ * product of the query with the prefix-decoded key; it is evaluated so that
+ * the sum is exact and only the final result is rounded:
+ *   - sigma_h = 31 - floor(log2 max_j |q_hj|) over the read channels (0 if
+ *     they are all zero), so that |q_hj| * 2^sigma_h < 2^32;
+ *   - per 64-token block b, E_b = f_b - 15 with f_b the largest binary16
+ *     exponent field among the read channels' scales in the block (at least
+ *     1, so subnormal and zero scales count as 2^-14): every read scale is
+ *     below 2^(E_b + 1);
+ *   - coefficient A_hjb = trunc(fl32(fl32(q_hj * 2^sigma_h) * scale_jb) *
+ *     2^-(E_b + 3)), an integer with |A| <= 2^30;
+ *   - with c' = c_t * 2^(4-t) (the prefix with zeros below it) and
+ *     d_j = 2^(4-t_j) - 16, the prefix key is (2 c' + d) * scale / 16, so
+ *     S_i = sum_j A_hjb * (2 c'_ij + d_j) is an exact integer and the score
+ *     is fl32(S_i * 2^(E_b - 1 - sigma_h)), one rounding to nearest even.
+ * Padding tokens are -inf.  Bound (vs the real dot product): at most
+ * 15 * (#read channels) * 2^(E_b - 1 - sigma_h) + 2^-24 * sum_j |q_hj k_ij|
+ * before the final rounding. */
+static int floor_log2_pos(double x) /* x > 0 */
+{
+    int e;
+    frexp(x, &e);
+    return e - 1;
+}
+
+void orc_scores(const uint64_t* planes, const uint16_t* scales, int64_t n, int D,
+                const uint8_t* depth, const float* q_used, int G, float* scores)
 {
     int64_t nb = (n + 63) / 64;
     int64_t npad = nb * 64;
+    int64_t* A = (int64_t*)malloc(sizeof(int64_t) * (size_t)D);
     for (int h = 0; h < G; ++h) {
-        for (int64_t i = 0; i < npad; ++i) {
-            if (i >= n) {
-                scores[(size_t)h * npad + i] = -INFINITY;
-                continue;
-            }
-            float acc = 0.0f;
+        const float* q = q_used + (size_t)h * D;
+        float qmax = 0.0f;
+        for (int j = 0; j < D; ++j)
+            if (depth[j] > 0 && fabsf(q[j]) > qmax) qmax = fabsf(q[j]);
+        int sigma = qmax > 0.0f ? 31 - floor_log2_pos((double)qmax) : 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            int ef = 1; /* largest exponent field of the read scales (subnormals and 0 count as 1) */
             for (int j = 0; j < D; ++j) {
-                int t = depth[j];
-                if (t == 0) continue;
-                int ct = orc_prefix_code(planes, nb, j, i, t);
-                float k = orc_dequant(ct, t, scales[(size_t)j * nb + i / 64]);
-                acc = fmaf(q_used[(size_t)h * D + j], k, acc);
+                int f = (scales[(size_t)j * nb + b] >> 10) & 31;
+                if (depth[j] > 0 && f > ef) ef = f;
             }
-            scores[(size_t)h * npad + i] = acc;
+            int E = ef - 15;
+            for (int j = 0; j < D; ++j) {
+                A[j] = 0;
+                if (depth[j] == 0) continue;
+                float qs = ldexpf(q[j], sigma);                 /* exact */
+                float pr = qs * orc_f16_to_f32(scales[(size_t)j * nb + b]); /* fl32 */
+                A[j] = (int64_t)truncf(ldexpf(pr, -(E + 3)));   /* exact scaling */
+            }
+            for (int i = 0; i < 64; ++i) {
+                int64_t tok = 64 * b + i;
+                if (tok >= n) {
+                    scores[(size_t)h * npad + tok] = -INFINITY;
+                    continue;
+                }
+                int64_t S = 0;
+                for (int j = 0; j < D; ++j) {
+                    int t = depth[j];
+                    if (t == 0) continue;
+                    int cp = orc_prefix_code(planes, nb, j, tok, t) << (4 - t);
+                    S += A[j] * (int64_t)(2 * cp + (1 << (4 - t)) - 16);
+                }
+                scores[(size_t)h * npad + tok] = (float)ldexp((double)S, E - 1 - sigma);
+            }
         }
     }
+    free(A);
 }
 
 /* The same sum in double (the real-valued definition, for tolerances). */
@@ -379,15 +420,15 @@ int orc_union(const int32_t* idx, int G, int k, int32_t* out)
     return len;
 }
 
-/* One decode step for one pair as the cpu baseline times it: plan, f32
- * scores, top-k per head and the union.  scores: [G][nb*64] scratch. */
+/* One decode step for one pair as the cpu baseline times it: plan, scores,
+ * top-k per head and the union.  scores: [G][nb*64] scratch. */
 int orc_step(const uint64_t* planes, const uint16_t* scales, int64_t n, int D, const float* q,
              const float* sigma2, const float* rot, int G, int budget, int mode, int k,
              uint8_t* depth, float* q_used, float* scores, int32_t* topk_idx, int32_t* union_idx)
 {
     int64_t npad = ((n + 63) / 64) * 64;
     orc_plan(q, sigma2, rot, G, D, budget, mode, depth, q_used);
-    orc_scores_f32(planes, scales, n, D, depth, q_used, G, scores);
+    orc_scores(planes, scales, n, D, depth, q_used, G, scores);
     for (int h = 0; h < G; ++h)
         orc_topk(scores + (size_t)h * npad, n, k, topk_idx + (size_t)h * k, NULL);
     return orc_union(topk_idx, G, k, union_idx);

@@ -126,7 +126,7 @@ struct ScanArgs {
     const float* q_used;
     int64_t stride;        // 1, or: scan one run of 32 consecutive blocks in every stride runs
     int64_t nlb;           // logical blocks per pair (rows of the STORE output / 64)
-    float* out;            // STORE: [P][G][nlb * 64]; LANEMAX: [P][G][nlb * (64 / TOK)]
+    float* out;            // STORE: [P][G][nlb * 64]; LANEMAX: [P][G][nlb * 4] (maxima of 16 tokens)
     const uint32_t* tau;   // FILTER: [P][G] key thresholds
     uint32_t* counts;      // FILTER: [P][G]
     uint64_t* cand;        // FILTER: [P][G][cap]
@@ -153,6 +153,7 @@ struct TopkLayout {
     int64_t sample_nlb;  // logical sample blocks per pair (whole runs)
     int64_t cap;         // candidate capacity per selection
     bool lanemax;        // fused threshold from per-lane maxima of the sample
+    int rank;            // fused threshold: this order statistic of the sample
     size_t off_tau, off_count, off_cand, off_sorted, bytes;  // top-k from given scores
     size_t off_list, off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };

@@ -8,21 +8,24 @@
 // exact answer with ties already broken.
 //
 // Pipeline per call (one selection = one (pair, head)):
-//  1. threshold: a lower bound of the k-th largest of a SAMPLE of scores
-//     (one run of 32 consecutive blocks in every `stride` runs; in the fused
-//     path, the maximum of each lane's 32 or 16 tokens of those blocks).
-//     Each sample value is a distinct token's score, so the k-th largest
-//     sample value -- and anything below it -- is a lower bound of the true
-//     k-th largest: every true winner passes it.  The bound used is the
-//     lower edge of the 22-bit key bin holding the sample's k-th largest.
+//  1. threshold: from a SAMPLE of scores (one run of 32 consecutive blocks
+//     in every `stride` runs; in the fused path, the maxima of groups of 16
+//     tokens of those blocks).  Each sample value is a distinct token's
+//     score.  From materialised scores the k-th largest sample value is
+//     used: a lower bound of the true k-th largest, so every true winner
+//     passes it.  The fused path uses the ceil(2k / stride)-th largest, which
+//     leaves about 2k candidates; should fewer than k pass, stage 3 selects
+//     that head over all of its scores.  The bound used is the lower edge of
+//     the 22-bit key bin holding the chosen sample value.
 //  2. filter:    one pass over all scores appends key >= threshold to a
-//                candidate list (wavefront-aggregated atomics).
+//                candidate list (workgroup-aggregated atomics; in the fused
+//                path, inside the scan).
 //  3. select:    exact k largest composites of the candidates (radix select
 //                with 11-bit digits, the last levels in LDS), each winner
 //                placed by its rank; a second rank by token index gives the
 //                winners sorted by index.  A selection whose candidates
-//                overflowed their capacity runs the same select directly over
-//                all its scores instead.
+//                overflowed their capacity, or number fewer than k, runs the
+//                same select directly over all its scores instead.
 //  4. union:     merge of the G index-sorted lists of a pair, duplicates
 //                dropped.
 #include "common.h"
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt,
 // The pairs with some head whose candidates overflowed their capacity, in
 // pair order: list[0] = how many, list[1..] = the pairs.  One workgroup.
 __global__ __launch_bounds__(kSelThreads) void overflow_list_kernel(const uint32_t* __restrict__ counts,
-                                                                   int P, int G, int64_t cap,
+                                                                   int P, int G, int64_t cap, int k,
                                                                    uint32_t* __restrict__ list)
 {
     __shared__ uint32_t wsum[kSelThreads / kWave];
@@ -425,7 +428,10 @@ __global__ __launch_bounds__(kSelThreads) void overflow_list_kernel(const uint32
         const int p = p0 + (int)threadIdx.x;
         bool f = false;
         if (p < P)
-            for (int h = 0; h < G; ++h) f |= (int64_t)counts[(size_t)p * G + h] > cap;
+            for (int h = 0; h < G; ++h) {
+                const int64_t c = counts[(size_t)p * G + h];
+                f |= c > cap || c < (int64_t)k;
+            }
         const uint64_t b = __ballot(f);
         if (lane == 0) wsum[wave] = (uint32_t)__popcll(b);
         __syncthreads();
@@ -518,7 +524,9 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_kernel(
     __shared__ SelShared sh;
     const int64_t m = blockIdx.x;
     const int64_t cnt = counts[m];
-    const bool dense = cnt > cap;
+    // too many candidates for the buffer, or (fused path) fewer than k
+    // above a statistical threshold: select over all scores instead
+    const bool dense = cnt > cap || cnt < (int64_t)k;
     if (!dense && cnt <= (int64_t)kRegSlots * blockDim.x) {
         // candidates read once into registers; the radix levels and the
         // winner gather run from there
@@ -707,9 +715,14 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k)
     int64_t s = 1;
     while ((s * 2) * (s * 2) * 4 * (int64_t)k <= n && s * 2 <= nb) s *= 2;
     L.stride = s;
-    // per-lane maxima (one value per 32 or 16 tokens) carry almost the same
-    // tail information as the tokens themselves once there are >= 4k of them
+    // maxima of groups of 16 tokens (four per block) carry almost the same
+    // tail information as the tokens themselves once there are >= 8k of them
     L.lanemax = n >= 128 * (int64_t)k * s;
+    // the fused threshold is the rank-th largest sample value: with one run
+    // in every s sampled, about rank * s >= 2k scores lie above it.  That is
+    // a statistical bound; a selection that ends up with fewer than k
+    // candidates is selected over all of its scores instead (stage 3).
+    L.rank = s == 1 ? k : (int)((2 * (int64_t)k + s - 1) / s);
     L.cap = 8 * (int64_t)k * s + 1024;
     if (L.cap > nb * 64) L.cap = nb * 64;
     L.sample_nlb = ((nb + 32 * s - 1) / (32 * s)) * 32;
@@ -786,9 +799,9 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         if ((e = launch_scan_args(a, P, G, L.lanemax ? 2 : 0, st)) != hipSuccess) return e;
         // every lane maximum is a distinct token's score, so the k-th largest
         // of them is still a lower bound of the k-th largest score
-        const int64_t row = L.sample_nlb * (L.lanemax ? (G <= 4 ? 2 : 4) : 64);
+        const int64_t row = L.sample_nlb * (L.lanemax ? 4 : 64);
         threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(sample, row, row, 1, row, row,
-                                                                     k, tau);
+                                                                     L.rank, tau);
     }
     if (stages & 2) {
         // filter: every block, keeping the scores at or above the threshold
@@ -804,7 +817,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
     }
     if (stages & 4) {
         // pairs whose candidates overflowed get their full scores recomputed
-        overflow_list_kernel<<<dim3(1), kSelThreads, 0, st>>>(counts, P, G, L.cap, list);
+        overflow_list_kernel<<<dim3(1), kSelThreads, 0, st>>>(counts, P, G, L.cap, k, list);
         a = base;
         a.stride = 1;
         a.nlb = nb;

@@ -162,7 +162,7 @@ def test_scan_bit_exact_and_within_tolerance(F, orc, n, D, G, mode, budget):
     for p in range(P):
         rp, rs = orc.pack(x[p])
         rd, _, rq = orc.plan(q[p], s2[p], budget, mode)
-        ref = orc.scores_f32(rp, rs, n, rd, rq)
+        ref = orc.scores(rp, rs, n, rd, rq)
         assert np.array_equal(scores[p].view(np.uint32), ref.view(np.uint32))
         d64 = orc.ref64.scores_def(rp, rs, n, rd, rq)
         assert np.all(np.abs(scores[p][:, :n] - d64) <= score_tol(d64, rq, rs))

@@ -311,7 +311,7 @@ def test_full_budget_is_full_4bit_dot(orc):
     n = 200
     x, planes, scales, q = _rand_index(orc, n, 40)
     depth = np.full(128, 4, np.uint8)
-    s32 = orc.scores_f32(planes, scales, n, depth, q)
+    s32 = orc.scores(planes, scales, n, depth, q)
     codes = orc.ref64.decode_codes(planes, n)
     sc = orc.ref64.f16_bits_to_f64(scales)[:, np.arange(n) // 64]
     k4 = (codes - 7.5) * sc / 8
@@ -331,28 +331,75 @@ def test_single_channel_single_plane_by_hand(orc):
     q[:, 3] = [1.0, -2.0, 0.5, 3.0]
     depth = np.zeros(128, np.uint8)
     depth[3] = 1
-    s = orc.scores_f32(planes, scales, n, depth, q)
+    s = orc.scores(planes, scales, n, depth, q)
     half = np.float32(orc.f16_bits_to_f32(scales[3, 0]) / 2)  # +-4 cells
     sign = np.where(x[:, 3] >= 0, 1.0, -1.0)
     assert np.array_equal(s[:, :n], (q[:, 3:4] * sign[None, :] * half).astype(np.float32))
 
 
-def test_scores_f32_contract_exact_on_tiny(orc):
-    n = 70
-    x, planes, scales, q = _rand_index(orc, n, 41)
-    depth = np.zeros(128, np.uint8)
-    depth[[1, 5, 9, 40, 77, 100, 127]] = [4, 1, 2, 3, 1, 4, 2]
-    s32 = orc.scores_f32(planes, scales, n, depth, q)
-    codes = orc.ref64.decode_codes(planes, n)
-    for h in (0, 3):
-        for i in (0, 33, 64, 69):
-            acc = np.float32(0)
-            for j in np.nonzero(depth)[0]:
-                t = int(depth[j])
-                kh = np.float32(orc.ref64.dequant(codes[j, i] >> (4 - t), t,
-                                                  orc.f16_bits_to_f32(scales[j, i // 64])))
-                acc = fma32(q[h, j], kh, acc)
-            assert s32[h, i] == acc
+def _def_and_bound(orc, planes, scales, n, depth, q):
+    """float64 definition and the contract's stated error bound before the
+    final rounding: 15 * (#read channels) * 2^(E_b - 1 - sigma_h) per block
+    plus 2^-24 * sum_j |q_hj k_ij|."""
+    ref = orc.ref64.scores_def(planes, scales, n, depth, q)
+    k = orc.ref64.dequant_keys(planes, scales, n, depth)  # [D][n] prefix keys
+    read = np.nonzero(depth)[0]
+    qmax = np.abs(q[:, read]).max(1)
+    sigma = np.where(qmax > 0, 31 - np.floor(np.log2(np.where(qmax > 0, qmax, 1))), 0)
+    ef = np.maximum(1, (scales[read] >> 10) & 31).max(0)  # [nb]
+    E = ef.astype(np.float64) - 15
+    unit = np.exp2(E[np.arange(n) // 64][None, :] - 1 - sigma[:, None])
+    bound = 15 * read.size * unit + 2.0 ** -24 * (np.abs(q[:, read, None]) * np.abs(k[read][None, :, :])).sum(1)
+    return ref, bound
+
+
+def test_fixed_point_scores_within_their_bound(orc):
+    # the exact-integer contract differs from the real dot product only by
+    # the coefficient truncation (bounded above) and one final rounding
+    for seed, B, mag in ((41, 48, 1.0), (44, 136, 1.0), (45, 512, 1.0), (46, 7, 1.0), (50, 48, 1e-3)):
+        n = 300
+        x, planes, scales, q = _rand_index(orc, n, seed)
+        if mag != 1.0:  # small keys: block scales far below 1 (binary16 exponent field ~ 5)
+            planes, scales = orc.pack(x * np.float32(mag))
+        s2 = np.exp(np.random.default_rng(seed).standard_normal(128)).astype(np.float32)
+        depth, _, qu = orc.plan(q, s2, B)
+        s = orc.scores(planes, scales, n, depth, qu)[:, :n].astype(np.float64)
+        ref, bound = _def_and_bound(orc, planes, scales, n, depth, qu)
+        assert np.all(np.abs(s - ref) <= bound + np.abs(ref) * 2.0 ** -24)
+
+
+def test_fixed_point_exact_when_representable(orc):
+    # power-of-two queries and scales with a short mantissa make every
+    # coefficient an exact integer: the score is the real dot product
+    # rounded once (here exactly representable)
+    n = 128
+    g = np.random.default_rng(47)
+    scales_pow = np.exp2(g.integers(-3, 4, 128)).astype(np.float32)
+    x = (g.standard_normal((n, 128)) * scales_pow).astype(np.float32)
+    planes, scales = orc.pack(x)
+    scales = (scales & np.uint16(0xFE00)).astype(np.uint16)  # 2 mantissa bits left
+    q = (np.exp2(g.integers(-4, 3, (4, 128))) * g.choice([-1, 1], (4, 128))).astype(np.float32)
+    depth = g.integers(0, 5, 128).astype(np.uint8)
+    s = orc.scores(planes, scales, n, depth, q)[:, :n].astype(np.float64)
+    ref = orc.ref64.scores_def(planes, scales, n, depth, q)
+    assert np.array_equal(s, ref.astype(np.float32).astype(np.float64))
+
+
+def test_fixed_point_scale_invariance_and_block_locality(orc):
+    n = 256
+    x, planes, scales, q = _rand_index(orc, n, 48)
+    depth = np.random.default_rng(49).integers(0, 5, 128).astype(np.uint8)
+    s = orc.scores(planes, scales, n, depth, q)
+    # a power-of-two query scale moves sigma and nothing else
+    s8 = orc.scores(planes, scales, n, depth, q * np.float32(8))
+    assert np.array_equal(s8[:, :n], (s[:, :n] * np.float32(8)))
+    # block 2's scales do not enter the scores of blocks 0, 1 and 3
+    sc2 = scales.copy()
+    sc2[:, 2] = (sc2[:, 2].astype(np.int32) + 1024).astype(np.uint16)  # one binade up
+    s2 = orc.scores(planes, sc2, n, depth, q)
+    keep = np.r_[0:128, 192:256]
+    assert np.array_equal(s2[:, keep], s[:, keep])
+    assert not np.array_equal(s2[:, 128:192], s[:, 128:192])
 
 
 def test_scores_within_tolerance_of_definition(orc):
@@ -360,7 +407,7 @@ def test_scores_within_tolerance_of_definition(orc):
     x, planes, scales, q = _rand_index(orc, n, 42)
     s2 = np.exp(np.random.default_rng(43).standard_normal(128)).astype(np.float32)
     depth, theta, qu = orc.plan(q, s2, 48)
-    s32 = orc.scores_f32(planes, scales, n, depth, qu)[:, :n]
+    s32 = orc.scores(planes, scales, n, depth, qu)[:, :n]
     ref = orc.ref64.scores_def(planes, scales, n, depth, qu)
     smax = orc.ref64.f16_bits_to_f64(scales).max()
     tol = 1e-5 * np.abs(ref) + 1e-6 * np.abs(qu).sum(1, keepdims=True) * smax
