@@ -1,7 +1,7 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
 Bit-exact: pack (planes, scales), plan (depths, level, active list, q_used),
-fp32 scores, top-k indices and values, union.  Scores are also checked against
+scores (the fixed-point contract), top-k indices and values, union.  Scores are also checked against
 the float64 definition: |s - s_def| <= 1e-5 |s_def| + 1e-6 ||q_h||_1 max scale.
 Inputs all come from the seeded generators in workloads/ or numpy.
 """
@@ -304,6 +304,60 @@ def test_fused_scan_topk_bit_exact(F, orc, kind, n, D, G, budget, k, mode):
             assert np.array_equal(val[p, h], ref["scores"][h][ref["topk"][h]])
         assert int(out.union_len[p]) == ref["union_len"]
         assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+
+
+def _sample_stride(n, k):
+    """One run of 32 blocks in every s runs is sampled for the fused
+    threshold: s is the largest power of two with (2s)^2 4k <= n kept."""
+    nb = (n + 63) // 64
+    s = 1
+    while (2 * s) ** 2 * 4 * k <= n and 2 * s <= nb:
+        s *= 2
+    return s
+
+
+def test_fused_fallback_when_the_sample_threshold_passes_too_few(F, orc):
+    """Keys planted in the first sampled run score far above everything else,
+    so the sample threshold (the ceil(2k/s)-th sampled score) leaves fewer
+    than k candidates for those heads.  Stage 3 must then select over every
+    score of the head: the result still equals the oracle bit for bit."""
+    P, G, D, n, k, budget = 2, 4, 128, 65536 + 300, 64, 48
+    g = np.random.default_rng(20261203)
+    scale = np.exp(0.7 * g.standard_normal(D)).astype(np.float32)
+    x = [(g.standard_normal((n, D)) * scale).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, 77)
+    rms = float(np.sqrt(np.mean(scale.astype(np.float64) ** 2)))
+    for p in range(P):
+        for h in range(G):
+            qh = q[p, h].astype(np.float64)
+            for i in range(12):  # distinct 16-token groups, all inside blocks 0..31
+                tok = 40 * (12 * h + i) + 3
+                x[p][tok] = (qh * (8.0 * rms / np.linalg.norm(qh))).astype(np.float32)
+    s = _sample_stride(n, k)
+    assert s > 1 and n < 128 * k * s  # token-level sample, one run in every s
+    rank = -(-2 * k // s)
+    say("fused fallback: planted sample winners", n, k, s)
+    planes, scales = F.pack(dev(np.stack(x)))
+    pl = F.plan(dev(q), dev(s2), budget, 0)
+    out = F.scan_topk(planes, scales, n, pl, k)
+    idx = out.idx.cpu().numpy()
+    val = out.val.cpu().numpy()
+    nb = (n + 63) // 64
+    sampled = np.zeros(n, bool)
+    for b0 in range(0, nb, 32 * s):
+        sampled[b0 * 64:min(n, (b0 + 32) * 64)] = True
+    short = 0
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        ref = orc.step(rp, rs, n, q[p], s2[p], budget, k)
+        for h in range(G):
+            sc = ref["scores"][h][:n]
+            thr = np.sort(sc[sampled])[::-1][rank - 1]
+            short += int((sc >= thr).sum() < k)
+            assert np.array_equal(idx[p, h], ref["topk"][h]), (p, h)
+            assert np.array_equal(val[p, h], sc[ref["topk"][h]])
+        assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+    assert short == P * G  # every head needed the fallback
 
 
 def test_host_resident_index_matches_device(F, orc):
