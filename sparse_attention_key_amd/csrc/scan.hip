@@ -52,14 +52,13 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kWaveBlocks = 64;                    // logical blocks per wavefront
-constexpr int kGroupBlocks = kWaves * kWaveBlocks;  // per workgroup
+constexpr int kGroupBlocks = 256;                  // logical blocks per workgroup
 constexpr int kRun = 32;                           // sampled blocks come in runs of 32
 constexpr int kSlotsMax = 128;
 constexpr int kRec = 32;                           // LDS bytes per (slot, half block) code record
 constexpr int kCodeBytes = 8 * 32 * kRec;          // 2 (4/C) half blocks x 32 C slots, every C
 constexpr int kCoefBytes = 4 * 32 * 16;            // (4/C) blocks x 32 C slots x 2 head pairs x 8 B
-constexpr int kStage = 32;                         // staged survivors per head and wavefront
+constexpr int kStage = 128;                        // staged survivors per wavefront (16-byte records)
 
 enum { kStore = 0, kFilter = 1, kLaneMax = 2 };
 
@@ -154,6 +153,7 @@ struct PairTables {
     uint32_t slot[kSlotsMax];                               // channel | depth << 8, deepest first
     __attribute__((aligned(8))) signed char d[kSlotsMax];   // 2^(4-t) - 16 per slot (0 past A)
     int sig[4 * GR];
+    float thr[4 * GR];                                      // FILTER: the heads' thresholds
     uint32_t qmax[4 * GR];
     uint32_t cnt[5];
 };
@@ -173,41 +173,63 @@ __device__ __forceinline__ int wave_max_dpp(int v)
 template <int GR, int MODE, int C>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const int G, const int A,
                                           const PairTables<GR>& T, unsigned char* code,
-                                          unsigned char* coef, uint64_t* stage, uint32_t* wcnt)
+                                          unsigned char* coef, v4i* stage)
 {
     constexpr int S = 32 * C, NB = 4 / C;
     constexpr int NH = 4 * GR;
+    constexpr int IB = kWaves * NB;  // logical blocks the workgroup takes per iteration
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int kap = lane >> 4, j16 = lane & 15;  // lane group (slot block / head) and row
     // block indices fit 32 bits (the host checks the index size)
     const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride;
-    const int lwave0 = ((int)blockIdx.x * kWaves + wave) * kWaveBlocks;  // first logical block
-    if (lwave0 >= nlb) return;
-    const int lend = min(lwave0 + kWaveBlocks, nlb);
+    // Iteration i of wavefront w takes logical blocks lg0 + i IB + w NB + (0 .. NB-1):
+    // at any time the four wavefronts of a workgroup read neighbouring blocks,
+    // so each 128-byte line of a plane row is used by all of them at once.
+    const int lg0 = (int)blockIdx.x * kGroupBlocks;
+    const int lgend = min(lg0 + kGroupBlocks, nlb);
+    if (lg0 + wave * NB >= lgend) return;
     const int64_t ldb = a.ldb;
+    const uint32_t ldb8 = (uint32_t)(ldb * 8);
 
-    // buffer descriptors of the pair's planes and scales
+    // the pair's planes and scales; the descriptors are rebased on every
+    // iteration's first physical block, so the range check stays exact
     const uint64_t* pplanes = a.planes + (size_t)p * a.D * 4 * ldb;
     const uint16_t* pscales = a.scales + (size_t)p * a.D * ldb;
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)pplanes, (short)0, (int)((int64_t)a.D * 4 * ldb * 8), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)pscales, (short)0, (int)((int64_t)a.D * ldb * 2), 0x00020000);
+    const uint32_t pbytes = (uint32_t)((int64_t)a.D * 4 * ldb * 8);
+    const uint32_t sbytes = (uint32_t)((int64_t)a.D * ldb * 2);
     constexpr uint32_t kOOB = 0x80000000u;  // past every record: the load returns 0
-    const uint32_t ldb8 = (uint32_t)(ldb * 8);
+    // (the record count is formed with a signed max: a saturating subtract
+    // would be computed per lane and turn the descriptor into a per-lane value)
+    auto records = [](uint32_t total, uint32_t off, bool live) {
+        return __builtin_amdgcn_readfirstlane(live ? max((int)total - (int)off, 0) : 0);
+    };
+    // plane s of a row is read at the row's plane-0 offset (per lane) plus
+    // s * ldb * 8 (the scalar offset); a lane whose block lies past the
+    // index is pointed out of range (see `mask_dead`), so no read ever leaves
+    // the pair's planes, whether or not the range check counts the scalar offset
+    auto plane_rsrc = [&](int pb0, bool live) {
+        const uint32_t off = (uint32_t)pb0 * 8u;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)pplanes + off), (short)0,
+                                                 records(pbytes, off, live), 0x00020000);
+    };
+    auto scale_rsrc = [&](int pb0, bool live) {
+        const uint32_t off = (uint32_t)pb0 * 2u;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)pscales + off), (short)0,
+                                                 records(sbytes, off, live), 0x00020000);
+    };
 
     // ---- codes: at step u the wavefront extracts slots 8C u .. 8C u + 8C-1
     // of every half block; lane L takes slot 8C u + L % 8C, half (L / 8C) % 2
     // of block L / 16C
     const int tsl = lane % (8 * C), ths = (lane / (8 * C)) & 1, tbk = lane / (16 * C);
-    uint32_t trow[4];  // plane-0 byte offset of the task's row (+ half), or out of range
+    uint32_t trow[4];  // byte offset of the task's plane-0 word from the iteration's first block
     int tt[4], tmax[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int e = 8 * C * u + tsl;
         tt[u] = (int)(T.slot[e] >> 8);
-        trow[u] = tt[u] ? (uint32_t)(T.slot[e] & 255u) * 4u * ldb8 + (uint32_t)ths * 4u : kOOB;
+        trow[u] = tt[u] ? (uint32_t)(T.slot[e] & 255u) * 4u * ldb8 + (uint32_t)tbk * 8u + (uint32_t)ths * 4u : kOOB;
         tmax[u] = __builtin_amdgcn_readfirstlane((int)(T.slot[8 * C * u] >> 8));  // deepest at step u
     }
     // record write offsets: chunk rho of step u goes to wr[(rho + C u) & 3] + u * 8C * 32
@@ -232,13 +254,13 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     // head pair) rows pi = L % 16C + 16C k, k = 0..3 (slot pi / 2, pair L & 1)
     constexpr int LPB = 16 * C;
     const int rb = lane / LPB, rl = lane % LPB, rhp = lane & 1;
-    uint32_t srow[4];  // scale row byte offset of slot k (out of range past A)
+    uint32_t srow[4];  // scale byte offset of slot k from the iteration's first block (out of range past A)
     float qt[4][GR][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int e = (rl >> 1) + 8 * C * k;
         const int j = (int)(T.slot[e] & 255u);
-        srow[k] = e < A ? (uint32_t)j * (uint32_t)(ldb * 2) : kOOB;
+        srow[k] = e < A ? (uint32_t)j * (uint32_t)(ldb * 2) + (uint32_t)rb * 2u : kOOB;
 #pragma unroll
         for (int gr = 0; gr < GR; ++gr)
 #pragma unroll
@@ -275,7 +297,42 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                                  : __uint_as_float(__float_as_uint(th) + 1u);
         }
     }
-    if (MODE == kFilter && lane < NH) wcnt[lane] = 0u;
+    // FILTER: screened tokens wait in this wavefront's stage as (exact sum,
+    // token, head | exponent << 16) records; a flush turns them into scores,
+    // keeps those at or above their head's threshold, and appends them to the
+    // candidate lists with one fetch-and-add per head
+    uint32_t scnt = 0;  // wavefront-uniform
+    auto flush = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (uint32_t r0 = 0; r0 < scnt; r0 += kWave) {
+            const bool valid = r0 + (uint32_t)lane < scnt;
+            v4i rec = valid ? stage[r0 + lane] : (v4i){0, 0, 0, 0};
+            const int h = rec.w & 0xFF, zeta = rec.w >> 16;
+            const int64_t S = (int64_t)(((uint64_t)(uint32_t)rec.y << 32) | (uint32_t)rec.x);
+            const float sc = (float)__builtin_ldexp((double)S, zeta);
+            const bool keep = valid && sc >= T.thr[h];
+            const uint64_t cv = composite(score_key(sc), (uint32_t)rec.z);
+            uint32_t nh = 0, mine = 0;
+            uint64_t mh[NH];
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+                mh[hh] = __builtin_amdgcn_ballot_w64(keep && h == hh);
+                if (lane == hh) nh = (uint32_t)__popcll(mh[hh]);
+                if (h == hh) mine = (uint32_t)__popcll(mh[hh] & lanes_below(lane));
+            }
+            uint32_t base = 0;
+            if (lane < NH && lane < G && nh) base = atomicAdd(&a.counts[(size_t)p * G + lane], nh);
+            const uint32_t bh = (uint32_t)__shfl((int)base, h, kWave);
+            if (keep && (int64_t)(bh + mine) < a.cap) a.cand[((size_t)p * G + h) * a.cap + bh + mine] = cv;
+        }
+        scnt = 0;
+    };
+    // lanes of existing heads, per head group
+    uint64_t hmask[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) hmask[gr] = __builtin_amdgcn_ballot_w64(kap + 4 * gr < G);
     // token offset (within its block) of this lane's column in chunk rho
     int toff[4];
 #pragma unroll
@@ -284,73 +341,120 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
         const int g = x < 4 ? (rho == 0 ? 3 : rho - 1) : (rho == 0 ? 7 : rho + 3);
         toff[rho] = 32 * (j16 >> 3) + g + 8 * (x & 3);
     }
+    // digit-tile read offset (block 0) of read r
+    uint32_t arow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) arow[r] = (uint32_t)(((32 * r + 8 * kap + (j16 >> 1)) * 2 + (j16 & 1)) * 8);
 
     // physical block of a logical one: runs of kRun, one run in every stride.
     // The NB blocks of an iteration lie in one run, so they are consecutive;
     // blocks past the index read as zeros (the buffer bound) and are masked.
-    auto phys = [&](int lb) { return (lb / kRun) * kRun * stride + (lb % kRun); };
-    auto issue = [&](int lb0, uint32_t (&w)[4][4], uint32_t (&scl)[4]) {
-        const uint32_t pb0 = (uint32_t)phys(lb0);
-        const uint32_t pb8 = (pb0 + (uint32_t)tbk) * 8u;
+    auto phys = [&](int lb) { return __builtin_amdgcn_readfirstlane((lb / kRun) * kRun * stride + (lb % kRun)); };
+    // per-lane offset of plane s of step u; a plane the slot does not read
+    // gets bit 31 set, which is out of range (kept in vector registers: a
+    // per-plane lane mask would take scalar registers for the whole loop)
+    uint32_t vo[4][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                w[u][s] = 0;
-                if (s < tmax[u]) {
-                    const uint32_t off = s < tt[u] ? trow[u] + (uint32_t)s * ldb8 + pb8 : kOOB;
-                    w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 0);
-                }
-            }
+        for (int s = 0; s < 4; ++s) {
+            vo[u][s] = trow[u] | (~(uint32_t)(s - tt[u]) & kOOB);
+            asm volatile("" : "+v"(vo[u][s]));
+        }
+    auto voff = [&](int u, int s) { return vo[u][s]; };
+    // blocks at or past the end of the index: their lanes read nothing from
+    // here on (only the last iterations of a pair have such blocks)
+    auto mask_dead = [&](int pb0) {
+        if (pb0 + NB > nbk) {
+            const uint32_t dead = tbk < nbk - pb0 ? 0u : kOOB;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            scl[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, srow[k] + (pb0 + (uint32_t)rb) * 2u, 0, 0) & 0xFFFFu;
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) vo[u][s] |= dead;
+        }
     };
 
-    uint32_t wn[4][4], scn[4];
-    issue(lwave0, wn, scn);
-    for (int lb0 = lwave0; lb0 < lend; lb0 += NB) {
-        uint32_t w[4][4], scl[4];
+    // the products of block b of the current iteration (digits and codes in LDS)
+    auto products = [&](int b, v4i (&kk)[GR], v4i (&o)[4][GR]) {
+        v2i ac[GR][4];
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ac[gr][r] = r < C ? tr8(coef + gr * kCoefBytes, (uint32_t)(b * (S * 16)) + arow[r]) : (v2i){0, 0};
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) kk[gr] = mfma_k(ac[gr], dcol, C);
+        v2i bc[4][4];
+#pragma unroll
+        for (int rho = 0; rho < 4; ++rho)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                bc[rho][r] = r < C ? tr8(code, rd[r][(rho + b) & 3] + (uint32_t)(2 * b * S * kRec)) : (v2i){0, 0};
+#pragma unroll
+        for (int rho = 0; rho < 4; ++rho)
+#pragma unroll
+            for (int gr = 0; gr < GR; ++gr) o[rho][gr] = mfma_k(ac[gr], bc[rho], C);
+    };
+    // Screen, per tile rho: a token whose exact S passes has fl(hi) >= hv =
+    // 2^(rho-1) (P - K) / 2^16 - bound(lo), with P = pred(th) 2^-zeta; hv is
+    // a float lower bound of that.
+    auto screen = [&](const v4i (&kk)[GR], int Eb, float (&hv)[GR][4]) {
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+            const float phi = __builtin_ldexpf(pth[gr], sig[gr] - 15 - Eb);
+            const float z = phi - (float)(kk[gr].z + kk[gr].w * 256);
+            const float zf = z - lob - 4.0f - fabsf(z) * (1.0f / 262144.0f);
+#pragma unroll
+            for (int rho = 0; rho < 4; ++rho)
+                hv[gr][rho] = __builtin_fmaf(zf, rho == 0 ? 0.5f : (float)(1 << (rho - 1)),
+                                             -(lob * (float)(1 << rho) + 2.0f));
+        }
+    };
+
+    // Loads run one iteration ahead, into the registers just consumed: the
+    // scales are used (and the next ones requested) first, then each plane
+    // word, replaced by the next iteration's as soon as it is extracted.  An
+    // iteration's first wait (for its scales) then covers only loads issued
+    // before the previous iteration's products.
+    auto issue_scales = [&](int pb0, bool live, uint32_t (&sn)[4]) {
+        const __amdgpu_buffer_rsrc_t rs = scale_rsrc(pb0, live);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sn[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, srow[k], 0, 0);
+    };
+    uint32_t w[4][4] = {}, sc[4];
+    int lb0 = lg0 + wave * NB;
+    {
+        const int pb0 = phys(lb0);
+        mask_dead(pb0);
+        const __amdgpu_buffer_rsrc_t r = plane_rsrc(pb0, true);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) w[u][s] = wn[u][s];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) scl[k] = scn[k];
-        if (lb0 + NB < lend) issue(lb0 + NB, wn, scn);  // next iteration's loads in flight
-
-        int pbk[NB], nval[NB];  // physical block, and its valid tokens (0 for dead blocks)
+            for (int s = 0; s < 4; ++s)
+                if (s < tmax[u]) w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(r, voff(u, s), (int)(s * ldb8), 0);
+        issue_scales(pb0, true, sc);
+    }
+    for (; lb0 < lgend; lb0 += IB) {
+        const int lbn = lb0 + IB;
+        const bool more = lbn < lgend;
+        const int pb0 = phys(lb0), pbn = more ? phys(lbn) : 0;  // past the end: zero records, nothing is read
+        int nval[NB];  // valid tokens of block b (0 for dead blocks)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int lb = lb0 + b;
-            pbk[b] = phys(lb);
-            const int64_t left = a.n - (int64_t)pbk[b] * 64;
-            nval[b] = (lb < nlb && pbk[b] < nbk) ? (int)(left < 64 ? left : 64) : 0;
+            const int64_t left = a.n - (int64_t)(pb0 + b) * 64;
+            nval[b] = (lb0 + b < nlb && pb0 + b < nbk) ? (int)(left < 64 ? left : 64) : 0;
         }
 
-        // ---- codes to LDS (a step with no slot to read is skipped: its
-        // records meet zero coefficients)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (tmax[u] == 0) continue;
-            v2i ch[4];
-            extract(w[u], tmax[u], ch);
-#pragma unroll
-            for (int rho = 0; rho < 4; ++rho)
-                *(v2i*)(code + wr[(rho + C * u) & 3] + u * 8 * C * kRec) = ch[rho];
-        }
-
-        // ---- block exponents: largest exponent field of the read scales (>= 1),
-        // reduced over the lanes of the block's row group
-        int ef = 1;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) ef = max(ef, (int)((scl[k] >> 10) & 31u));
-        ef = max(ef, __builtin_amdgcn_update_dpp(0, ef, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-        ef = max(ef, __builtin_amdgcn_update_dpp(0, ef, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-        ef = max(ef, __builtin_amdgcn_update_dpp(0, ef, 0x141, 0xF, 0xF, false));  // row_half_mirror
-        ef = max(ef, __builtin_amdgcn_update_dpp(0, ef, 0x140, 0xF, 0xF, false));  // row_mirror
-        if (C >= 2) ef = max(ef, __shfl_xor(ef, 16, kWave));
-        if (C >= 4) ef = max(ef, __shfl_xor(ef, 32, kWave));
+        // ---- block exponents: largest exponent field of the read scales (>= 1);
+        // fp16 bit patterns of non-negative values order like the values
+        uint32_t mx = max(max(sc[0], sc[1]), max(sc[2], sc[3])) & 0xFFFFu;
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x141, 0xF, 0xF, false));  // row_half_mirror
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xF, 0xF, false));  // row_mirror
+        if (C >= 2) mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, kWave));
+        if (C >= 4) mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, kWave));
+        const int ef = max(1, (int)(mx >> 10) & 31);
         int Eb[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) Eb[b] = __builtin_amdgcn_readlane(ef, b * LPB) - 15;
@@ -362,14 +466,14 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int e = (rl >> 1) + 8 * C * k;
-                const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)scl[k]);
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
 #pragma unroll
                 for (int gr = 0; gr < GR; ++gr) {
                     uint32_t dig[2];
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
                         // trunc(fl32(q 2^sigma * scale) 2^-(E+3)); q 2^sigma 2^-(E+3) is exact
-                        const int Ai = (int)((qt[k][gr][x] * pw) * sc);
+                        const int Ai = (int)((qt[k][gr][x] * pw) * sf);
                         dig[x] = ((uint32_t)Ai + 0x00808080u) ^ 0x00808080u;
                     }
                     *(v2i*)(coef + gr * kCoefBytes + rb * (S * 16) + (e * 2 + rhp) * 8) =
@@ -377,88 +481,94 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                 }
             }
         }
+        issue_scales(pbn, more, sc);
+        // ---- codes to LDS (a step with no slot to read is skipped: its
+        // records meet zero coefficients)
+        if (more) mask_dead(pbn);
+        const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pbn, more);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (tmax[u] == 0) continue;
+            v2i ch[4];
+            extract(w[u], tmax[u], ch);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (s < tmax[u]) w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(rn, voff(u, s), (int)(s * ldb8), 0);
+#pragma unroll
+            for (int rho = 0; rho < 4; ++rho)
+                *(v2i*)(code + wr[(rho + C * u) & 3] + u * 8 * C * kRec) = ch[rho];
+        }
+
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- products per block
+        // ---- products per block; block b+1's products are started before
+        // block b is screened, so they run under its screen and staging
+        v4i kkn[GR], on[4][GR];
+        products(0, kkn, on);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int lb = lb0 + b;
-            v2i ac[GR][4];
-#pragma unroll
-            for (int gr = 0; gr < GR; ++gr)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    ac[gr][r] = r < C ? tr8(coef + gr * kCoefBytes,
-                                            (uint32_t)(b * (S * 16) + ((32 * r + 8 * kap + (j16 >> 1)) * 2 + (j16 & 1)) * 8))
-                                      : (v2i){0, 0};
-            v4i kk[GR];
-            float hv[GR][4];
-            int64_t smax[GR];
+            v4i kk[GR], o[4][GR];
 #pragma unroll
             for (int gr = 0; gr < GR; ++gr) {
-                kk[gr] = mfma_k(ac[gr], dcol, C);
-                smax[gr] = INT64_MIN;
+                kk[gr] = kkn[gr];
+#pragma unroll
+                for (int rho = 0; rho < 4; ++rho) o[rho][gr] = on[rho][gr];
             }
-            v2i bc[4][4];
-#pragma unroll
-            for (int rho = 0; rho < 4; ++rho)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    bc[rho][r] = r < C ? tr8(code, rd[r][(rho + b) & 3] + (uint32_t)(2 * b * S * kRec))
-                                       : (v2i){0, 0};
-            v4i o[4][GR];
-#pragma unroll
-            for (int rho = 0; rho < 4; ++rho)
-#pragma unroll
-                for (int gr = 0; gr < GR; ++gr) o[rho][gr] = mfma_k(ac[gr], bc[rho], C);
+            if (b + 1 < NB) products(b + 1, kkn, on);
             if (MODE == kFilter) {
-                // Screen, per tile rho: a token whose exact S passes has
-                // fl(hi) >= hv = 2^(rho-1) (P - K) / 2^16 - bound(lo), with
-                // P = pred(th) 2^-zeta; hv is a float lower bound of that.
-#pragma unroll
-                for (int gr = 0; gr < GR; ++gr) {
-                    const float phi = __builtin_ldexpf(pth[gr], sig[gr] - 15 - Eb[b]);
-                    const float z = phi - (float)(kk[gr].z + kk[gr].w * 256);
-                    const float zf = z - lob - 4.0f - fabsf(z) * (1.0f / 262144.0f);
-#pragma unroll
-                    for (int rho = 0; rho < 4; ++rho)
-                        hv[gr][rho] = __builtin_fmaf(zf, rho == 0 ? 0.5f : (float)(1 << (rho - 1)),
-                                                     -(lob * (float)(1 << rho) + 2.0f));
-                }
-                const bool fullb = nval[b] == 64;
-                auto passes = [&](int rho, int gr) {
-                    const int hi = o[rho][gr].z + o[rho][gr].w * 256;
-                    return (float)hi >= hv[gr][rho] && (fullb || toff[rho] < nval[b]) && kap + 4 * gr < G;
-                };
-                bool any = false;
+                float hv[GR][4];
+                screen(kk, Eb[b], hv);
+                // lanes whose (head, token) passes the screen, as wavefront masks
+                uint64_t m[4][GR], mor = 0;
 #pragma unroll
                 for (int rho = 0; rho < 4; ++rho)
 #pragma unroll
-                    for (int gr = 0; gr < GR; ++gr) any |= passes(rho, gr);
-                if (any) {  // rare: exact scores of the survivors
+                    for (int gr = 0; gr < GR; ++gr) {
+                        m[rho][gr] = __builtin_amdgcn_ballot_w64((float)(o[rho][gr].z + o[rho][gr].w * 256) >=
+                                                                 hv[gr][rho]) & hmask[gr];
+                        mor |= m[rho][gr];
+                    }
+                if (mor) {  // rare: the exact sums of the screened tokens go to the stage
+                    if (nval[b] != 64) {  // the last block of a pair: drop its padding tokens
+                        mor = 0;
 #pragma unroll
-                    for (int rho = 0; rho < 4; ++rho)
+                        for (int rho = 0; rho < 4; ++rho) {
+                            const uint64_t vm = __builtin_amdgcn_ballot_w64(toff[rho] < nval[b]);
 #pragma unroll
-                        for (int gr = 0; gr < GR; ++gr) {
-                            if (!passes(rho, gr)) continue;
-                            const int h = kap + 4 * gr;
-                            const float sc = exact_score(o[rho][gr], recombine(kk[gr]), rho, Eb[b] - 1 - sig[gr]);
-                            if (sc >= thr[gr]) {
-                                const uint32_t tok = (uint32_t)pbk[b] * 64u + (uint32_t)toff[rho];
-                                const uint64_t cv = composite(score_key(sc), tok);
-                                const uint32_t pos = atomicAdd(&wcnt[h], 1u);
-                                if (pos < (uint32_t)kStage) {
-                                    stage[h * kStage + pos] = cv;
-                                } else {
-                                    const uint32_t slot = atomicAdd(&a.counts[(size_t)p * G + h], 1u);
-                                    if ((int64_t)slot < a.cap) a.cand[((size_t)p * G + h) * a.cap + slot] = cv;
-                                }
+                            for (int gr = 0; gr < GR; ++gr) {
+                                m[rho][gr] &= vm;
+                                mor |= m[rho][gr];
                             }
                         }
+                    }
+#pragma unroll
+                    for (int gr = 0; gr < GR; ++gr) {
+                        const int64_t Kc = recombine(kk[gr]);
+                        const uint32_t tag = (uint32_t)(kap + 4 * gr) | ((uint32_t)(Eb[b] - 1 - sig[gr]) << 16);
+#pragma unroll
+                        for (int rho = 0; rho < 4; ++rho) {
+                            const uint64_t mm = m[rho][gr];
+                            if (!mm) continue;
+                            const uint32_t np = (uint32_t)__popcll(mm);
+                            if (scnt + np > (uint32_t)kStage) flush();
+                            if ((mm >> lane) & 1u) {
+                                const int64_t x = recombine(o[rho][gr]);
+                                const int64_t S = (rho == 0 ? x * 2 : (x >> (rho - 1))) + Kc;
+                                const uint32_t tok = (uint32_t)(pb0 + b) * 64u + (uint32_t)toff[rho];
+                                stage[scnt + (uint32_t)__popcll(mm & lanes_below(lane))] =
+                                    (v4i){(int)(uint32_t)S, (int)(uint32_t)((uint64_t)S >> 32), (int)tok, (int)tag};
+                            }
+                            scnt += np;
+                        }
+                    }
                 }
             } else {
+                int64_t smax[GR];
+#pragma unroll
+                for (int gr = 0; gr < GR; ++gr) smax[gr] = INT64_MIN;
 #pragma unroll
                 for (int rho = 0; rho < 4; ++rho) {
                     const bool tval = toff[rho] < nval[b];
@@ -479,40 +589,24 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                         }
                     }
                 }
-            }
-            if (MODE == kLaneMax) {
-                // maxima of 16 tokens: lanes 4q .. 4q+3 of a head
+                if (MODE == kLaneMax) {
+                    // maxima of 16 tokens: lanes 4q .. 4q+3 of a head
 #pragma unroll
-                for (int gr = 0; gr < GR; ++gr) {
-                    float v = smax[gr] == INT64_MIN ? -INFINITY
-                            : (float)__builtin_ldexp((double)smax[gr], Eb[b] - 1 - sig[gr]);
-                    v = fmaxf(v, __shfl_xor(v, 1, kWave));
-                    v = fmaxf(v, __shfl_xor(v, 2, kWave));
-                    const int h = kap + 4 * gr;
-                    if ((j16 & 3) == 0 && h < G && lb < nlb)
-                        a.out[((size_t)p * G + h) * (a.nlb * 4) + (int64_t)lb * 4 + (j16 >> 2)] = v;
+                    for (int gr = 0; gr < GR; ++gr) {
+                        float v = smax[gr] == INT64_MIN ? -INFINITY
+                                : (float)__builtin_ldexp((double)smax[gr], Eb[b] - 1 - sig[gr]);
+                        v = fmaxf(v, __shfl_xor(v, 1, kWave));
+                        v = fmaxf(v, __shfl_xor(v, 2, kWave));
+                        const int h = kap + 4 * gr;
+                        if ((j16 & 3) == 0 && h < G && lb < nlb)
+                            a.out[((size_t)p * G + h) * (a.nlb * 4) + (int64_t)lb * 4 + (j16 >> 2)] = v;
+                    }
                 }
             }
         }
         __builtin_amdgcn_wave_barrier();  // the next iteration rewrites this wavefront's LDS
     }
-    if (MODE == kFilter) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint32_t nh = 0, base = 0;
-        if (lane < NH && lane < G) {
-            nh = min(wcnt[lane], (uint32_t)kStage);
-            if (nh) base = atomicAdd(&a.counts[(size_t)p * G + lane], nh);
-        }
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const uint32_t n_h = (uint32_t)__builtin_amdgcn_readlane((int)nh, h);
-            const uint32_t b_h = (uint32_t)__builtin_amdgcn_readlane((int)base, h);
-            if ((uint32_t)lane < n_h && (int64_t)(b_h + lane) < a.cap)
-                a.cand[((size_t)p * G + h) * a.cap + b_h + lane] = stage[h * kStage + lane];
-        }
-    }
+    if (MODE == kFilter && scnt) flush();
 }
 
 template <int GR, int MODE>
@@ -522,8 +616,7 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
     __shared__ PairTables<GR> T;
     __shared__ __attribute__((aligned(16))) unsigned char s_code[kWaves][kCodeBytes];
     __shared__ __attribute__((aligned(16))) unsigned char s_coef[kWaves][GR * kCoefBytes];
-    __shared__ uint64_t s_stage[kWaves][NH * kStage];
-    __shared__ uint32_t s_wcnt[kWaves][NH];
+    __shared__ v4i s_stage[MODE == kFilter ? kWaves : 1][MODE == kFilter ? kStage : 1];
 
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int A = a.n_active[p];
@@ -557,6 +650,12 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
             sg = 31 - ((int)((__float_as_uint(qq) >> 23) & 255u) - 127 - (sub ? 64 : 0));
         }
         T.sig[threadIdx.x] = sg;
+        float th = INFINITY;
+        if (MODE == kFilter && (int)threadIdx.x < G) {
+            const uint32_t tk = a.tau[(size_t)p * G + threadIdx.x];
+            th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
+        }
+        T.thr[threadIdx.x] = th;
     }
     __syncthreads();
     if (wave == 0) {  // slots of a depth class in ascending channel order
@@ -593,11 +692,10 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
 
     unsigned char* code = s_code[wave];
     unsigned char* coef = s_coef[wave];
-    uint64_t* stage = s_stage[wave];
-    uint32_t* wcnt = s_wcnt[wave];
-    if (A <= 32) scan_body<GR, MODE, 1>(a, p, G, A, T, code, coef, stage, wcnt);
-    else if (A <= 64) scan_body<GR, MODE, 2>(a, p, G, A, T, code, coef, stage, wcnt);
-    else scan_body<GR, MODE, 4>(a, p, G, A, T, code, coef, stage, wcnt);
+    v4i* stage = s_stage[MODE == kFilter ? wave : 0];
+    if (A <= 32) scan_body<GR, MODE, 1>(a, p, G, A, T, code, coef, stage);
+    else if (A <= 64) scan_body<GR, MODE, 2>(a, p, G, A, T, code, coef, stage);
+    else scan_body<GR, MODE, 4>(a, p, G, A, T, code, coef, stage);
 }
 
 // blockIdx.y is the pair; with a pair list (score mode only), the rows of
