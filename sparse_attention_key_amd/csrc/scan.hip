@@ -143,10 +143,19 @@ __device__ __forceinline__ void extract(const uint32_t (&w)[4], int tmax, v2i (&
 
 // LDS layout of the codes.  Record (block b, half hs, slot e) -- 32 bytes,
 // four 8-byte chunks rho of weight 2^rho -- sits at ((2b + hs) S + e) * 32,
-// and chunk rho at position (rho + skew) & 3 within it, skew = e + e/8 +
-// 2 hs + b: the 16 rows of a transposing read (8 slots x 2 halves) and the
-// 32 records written by half a wavefront then fall on distinct banks.
-__device__ __forceinline__ int rec_skew(int e, int hs, int b) { return (e + (e >> 3) + 2 * hs + b) & 3; }
+// and chunk rho at position (rho + skew) & 3 within it, skew = e + a (e/4)
+// + e/8 + 2 hs + b with a = 1 for C = 1 and 2 otherwise.  A 64-bit write
+// goes 16 lanes at a time to 32 banks and a transposing read 32 lanes at a
+// time to 64 banks (measured); with this skew the 16 records of a write
+// pass and the 32 rows of a read pass all fall on distinct banks.  Step u
+// of the writer holds slots 8 C u + tsl, whose skew is that of slot tsl
+// plus (2a + 1) C u.
+template <int C>
+__device__ __forceinline__ int rec_skew(int e, int hs, int b)
+{
+    return (e + (C == 1 ? 1 : 2) * (e >> 2) + (e >> 3) + 2 * hs + b) & 3;
+}
+template <int C> constexpr int kSkewStep = (C == 1 ? 3 : 5) * C;
 
 template <int GR>
 struct PairTables {
@@ -232,10 +241,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
         trow[u] = tt[u] ? (uint32_t)(T.slot[e] & 255u) * 4u * ldb8 + (uint32_t)tbk * 8u + (uint32_t)ths * 4u : kOOB;
         tmax[u] = __builtin_amdgcn_readfirstlane((int)(T.slot[8 * C * u] >> 8));  // deepest at step u
     }
-    // record write offsets: chunk rho of step u goes to wr[(rho + C u) & 3] + u * 8C * 32
+    // record write offsets: chunk rho of step u goes to wr[(rho + kSkewStep u) & 3] + u * 8C * 32
     uint32_t wr[4];
     {
-        const int sk = rec_skew(tsl, ths, tbk);
+        const int sk = rec_skew<C>(tsl, ths, tbk);
         const uint32_t base = (uint32_t)(((2 * tbk + ths) * S + tsl) * kRec);
 #pragma unroll
         for (int m = 0; m < 4; ++m) wr[m] = base + (uint32_t)(((m + sk) & 3) * 8);
@@ -245,7 +254,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 #pragma unroll
     for (int r = 0; r < C; ++r) {
         const int e = 32 * r + 8 * kap + (j16 >> 1), hs = j16 & 1;
-        const int sk = rec_skew(e, hs, 0);
+        const int sk = rec_skew<C>(e, hs, 0);
         const uint32_t base = (uint32_t)((hs * S + e) * kRec);
 #pragma unroll
         for (int m = 0; m < 4; ++m) rd[r][m] = base + (uint32_t)(((m + sk) & 3) * 8);
@@ -496,7 +505,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                 if (s < tmax[u]) w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(rn, voff(u, s), (int)(s * ldb8), 0);
 #pragma unroll
             for (int rho = 0; rho < 4; ++rho)
-                *(v2i*)(code + wr[(rho + C * u) & 3] + u * 8 * C * kRec) = ch[rho];
+                *(v2i*)(code + wr[(rho + kSkewStep<C> * u) & 3] + u * 8 * C * kRec) = ch[rho];
         }
 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
