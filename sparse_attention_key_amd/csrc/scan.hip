@@ -56,7 +56,7 @@ constexpr int kGroupBlocks = 256;                  // logical blocks per workgro
 constexpr int kRun = 32;                           // sampled blocks come in runs of 32
 constexpr int kSlotsMax = 128;
 constexpr int kRec = 32;                           // LDS bytes per (slot, half block) code record
-constexpr int kCodeBytes = 8 * 32 * kRec;          // 2 (4/C) half blocks x 32 C slots, every C
+constexpr int kCodeBytes = 8 * 32 * kRec + 8 * 32;   // 2 (4/C) half blocks of 32 C slots and a spare record
 constexpr int kCoefBytes = 4 * 32 * 16;            // (4/C) blocks x 32 C slots x 2 head pairs x 8 B
 constexpr int kStage = 128;                        // staged survivors per wavefront (16-byte records)
 
@@ -142,20 +142,18 @@ __device__ __forceinline__ void extract(const uint32_t (&w)[4], int tmax, v2i (&
 }
 
 // LDS layout of the codes.  Record (block b, half hs, slot e) -- 32 bytes,
-// four 8-byte chunks rho of weight 2^rho -- sits at ((2b + hs) S + e) * 32,
-// and chunk rho at position (rho + skew) & 3 within it, skew = e + a (e/4)
-// + e/8 + 2 hs + b with a = 1 for C = 1 and 2 otherwise.  A 64-bit write
-// goes 16 lanes at a time to 32 banks and a transposing read 32 lanes at a
-// time to 64 banks (measured); with this skew the 16 records of a write
-// pass and the 32 rows of a read pass all fall on distinct banks.  Step u
-// of the writer holds slots 8 C u + tsl, whose skew is that of slot tsl
-// plus (2a + 1) C u.
-template <int C>
-__device__ __forceinline__ int rec_skew(int e, int hs, int b)
-{
-    return (e + (C == 1 ? 1 : 2) * (e >> 2) + (e >> 3) + 2 * hs + b) & 3;
-}
-template <int C> constexpr int kSkewStep = (C == 1 ? 3 : 5) * C;
+// four 8-byte chunks rho of weight 2^rho -- sits at (2b + hs) H + 32 e with
+// H = 32 S + 32 (one spare record per half block), and chunk rho at
+// position (rho + skew) & 3 within it, skew = e + 2 (e/4) + 2 (e/8) +
+// 2 (b/2).  A 64-bit write goes 16 lanes at a time to 32 banks and a
+// transposing read 32 lanes at a time to 64 banks (measured); with this
+// layout the 16 records of a write pass (two slots x 8 half blocks, the
+// lane order that keeps loads contiguous) and the 32 rows of a read pass
+// all fall on distinct banks.  Step u of the writer holds slots 8 C u +
+// tsl, whose skew is that of slot tsl plus 2 C u.
+__device__ __forceinline__ int rec_skew(int e, int b) { return (e + 2 * (e >> 2) + 2 * (e >> 3) + 2 * (b >> 1)) & 3; }
+template <int C> constexpr int kHalfBytes = 32 * 32 * C + 32;
+template <int C> constexpr int kSkewStep = 2 * C;
 
 template <int GR>
 struct PairTables {
@@ -229,9 +227,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     };
 
     // ---- codes: at step u the wavefront extracts slots 8C u .. 8C u + 8C-1
-    // of every half block; lane L takes slot 8C u + L % 8C, half (L / 8C) % 2
-    // of block L / 16C
-    const int tsl = lane % (8 * C), ths = (lane / (8 * C)) & 1, tbk = lane / (16 * C);
+    // of every half block; lane L takes slot 8C u + L / 2NB, block (L / 2) %
+    // NB, half L % 2, so neighbouring lanes read neighbouring words of a row
+    const int tsl = lane / (2 * NB), tbk = (lane / 2) % NB, ths = lane & 1;
     uint32_t trow[4];  // byte offset of the task's plane-0 word from the iteration's first block
     int tt[4], tmax[4];
 #pragma unroll
@@ -244,18 +242,18 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     // record write offsets: chunk rho of step u goes to wr[(rho + kSkewStep u) & 3] + u * 8C * 32
     uint32_t wr[4];
     {
-        const int sk = rec_skew<C>(tsl, ths, tbk);
-        const uint32_t base = (uint32_t)(((2 * tbk + ths) * S + tsl) * kRec);
+        const int sk = rec_skew(tsl, tbk);
+        const uint32_t base = (uint32_t)((2 * tbk + ths) * kHalfBytes<C> + tsl * kRec);
 #pragma unroll
         for (int m = 0; m < 4; ++m) wr[m] = base + (uint32_t)(((m + sk) & 3) * 8);
     }
-    // transposing read offsets: read r of tile (b, rho) is rd[r][(rho + b) & 3] + 2 b S 32
+    // transposing read offsets: read r of tile (b, rho) is rd[r][(rho + 2 (b/2)) & 3] + 2 b H
     uint32_t rd[C][4];
 #pragma unroll
     for (int r = 0; r < C; ++r) {
         const int e = 32 * r + 8 * kap + (j16 >> 1), hs = j16 & 1;
-        const int sk = rec_skew<C>(e, hs, 0);
-        const uint32_t base = (uint32_t)((hs * S + e) * kRec);
+        const int sk = rec_skew(e, 0);
+        const uint32_t base = (uint32_t)(hs * kHalfBytes<C> + e * kRec);
 #pragma unroll
         for (int m = 0; m < 4; ++m) rd[r][m] = base + (uint32_t)(((m + sk) & 3) * 8);
     }
@@ -398,7 +396,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
         for (int rho = 0; rho < 4; ++rho)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                bc[rho][r] = r < C ? tr8(code, rd[r][(rho + b) & 3] + (uint32_t)(2 * b * S * kRec)) : (v2i){0, 0};
+                bc[rho][r] = r < C ? tr8(code, rd[r][(rho + 2 * (b >> 1)) & 3] + (uint32_t)(2 * b * kHalfBytes<C>))
+                                   : (v2i){0, 0};
 #pragma unroll
         for (int rho = 0; rho < 4; ++rho)
 #pragma unroll
