@@ -132,6 +132,7 @@ struct ScanArgs {
     uint64_t* cand;        // FILTER: [P][G][cap]
     int64_t cap;
     const uint32_t* list;  // optional (score mode): list[0] pairs listed in list[1..]; only they are scanned
+    int gb;                // logical blocks per workgroup (set by the launcher)
 };
 constexpr int kListRows = 4;  // workgroup rows that walk a pair list
 // mode: 0 store scores, 1 filter into candidates, 2 per-lane maxima

@@ -52,7 +52,7 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kGroupBlocks = 256;                  // logical blocks per workgroup
+constexpr int kGroupBlocks = 256;                  // logical blocks per workgroup (at most)
 constexpr int kRun = 32;                           // sampled blocks come in runs of 32
 constexpr int kSlotsMax = 128;
 constexpr int kRec = 32;                           // LDS bytes per (slot, half block) code record
@@ -193,8 +193,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     // Iteration i of wavefront w takes logical blocks lg0 + i IB + w NB + (0 .. NB-1):
     // at any time the four wavefronts of a workgroup read neighbouring blocks,
     // so each 128-byte line of a plane row is used by all of them at once.
-    const int lg0 = (int)blockIdx.x * kGroupBlocks;
-    const int lgend = min(lg0 + kGroupBlocks, nlb);
+    const int lg0 = (int)blockIdx.x * a.gb;
+    const int lgend = min(lg0 + a.gb, nlb);
     if (lg0 + wave * NB >= lgend) return;
     const int64_t ldb = a.ldb;
     const uint32_t ldb8 = (uint32_t)(ldb * 8);
@@ -574,37 +574,41 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                     }
                 }
             } else {
-                int64_t smax[GR];
+                if (MODE == kStore) {
 #pragma unroll
-                for (int gr = 0; gr < GR; ++gr) smax[gr] = INT64_MIN;
+                    for (int rho = 0; rho < 4; ++rho) {
+                        const bool tval = toff[rho] < nval[b];
 #pragma unroll
-                for (int rho = 0; rho < 4; ++rho) {
-                    const bool tval = toff[rho] < nval[b];
-#pragma unroll
-                    for (int gr = 0; gr < GR; ++gr) {
-                        const int h = kap + 4 * gr;
-                        const int64_t Kc = recombine(kk[gr]);
-                        if (MODE == kStore) {
-                            const float sc = exact_score(o[rho][gr], Kc, rho, Eb[b] - 1 - sig[gr]);
+                        for (int gr = 0; gr < GR; ++gr) {
+                            const int h = kap + 4 * gr;
+                            const float sc = exact_score(o[rho][gr], recombine(kk[gr]), rho, Eb[b] - 1 - sig[gr]);
                             if (h < G && lb < nlb)
                                 a.out[((size_t)p * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
                                     tval ? sc : -INFINITY;
-                        } else {
-                            // the block's tokens share zeta: the largest S has the largest score
-                            const int64_t x = recombine(o[rho][gr]);
-                            const int64_t Sv = (rho == 0 ? x * 2 : (x >> (rho - 1))) + Kc;
-                            if (tval && Sv > smax[gr]) smax[gr] = Sv;
                         }
                     }
-                }
-                if (MODE == kLaneMax) {
-                    // maxima of 16 tokens: lanes 4q .. 4q+3 of a head
+                } else {
+                    // Maxima of 16 tokens from the top two digit rows (S ~ 2^(17-rho)
+                    // hi + K): the sample is only a statistic for the threshold, whose
+                    // exactness the candidate count check keeps, so an estimate
+                    // within a few units in 2^16 of the exact sum serves.
 #pragma unroll
                     for (int gr = 0; gr < GR; ++gr) {
-                        float v = smax[gr] == INT64_MIN ? -INFINITY
-                                : (float)__builtin_ldexp((double)smax[gr], Eb[b] - 1 - sig[gr]);
-                        v = fmaxf(v, __shfl_xor(v, 1, kWave));
-                        v = fmaxf(v, __shfl_xor(v, 2, kWave));
+                        const float Kf = __builtin_fmaf((float)(kk[gr].z + kk[gr].w * 256), 65536.0f,
+                                                        (float)(kk[gr].x + kk[gr].y * 256));
+                        float v = -INFINITY;
+#pragma unroll
+                        for (int rho = 0; rho < 4; ++rho) {
+                            const float e = __builtin_fmaf((float)(o[rho][gr].z + o[rho][gr].w * 256),
+                                                           (float)(1 << (17 - rho)), Kf);
+                            v = nval[b] == 64 || toff[rho] < nval[b] ? fmaxf(v, e) : v;
+                        }
+                        v = __builtin_ldexpf(v, Eb[b] - 1 - sig[gr]);
+                        // lanes 4q .. 4q+3 of a head hold one group of 16 tokens
+                        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+                        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
                         const int h = kap + 4 * gr;
                         if ((j16 & 3) == 0 && h < G && lb < nlb)
                             a.out[((size_t)p * G + h) * (a.nlb * 4) + (int64_t)lb * 4 + (j16 >> 2)] = v;
@@ -723,10 +727,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a, int G)
 }
 
 template <int MODE>
-hipError_t launch_mode(const ScanArgs& a, int P, int G, hipStream_t st)
+hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
 {
+    ScanArgs a = args;
     const int rows = a.list ? (P < kListRows ? P : kListRows) : P;
-    dim3 grid((unsigned)((a.nlb + kGroupBlocks - 1) / kGroupBlocks), (unsigned)rows);
+    // blocks per workgroup: 256, or fewer (a multiple of every iteration's
+    // 16 blocks) when that leaves too few workgroups to fill the chip twice
+    a.gb = kGroupBlocks;
+    while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < 2048) a.gb /= 2;
+    dim3 grid((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)rows);
     if (G <= 4) scan_kernel<1, MODE><<<grid, kThreads, 0, st>>>(a, G);
     else scan_kernel<2, MODE><<<grid, kThreads, 0, st>>>(a, G);
     return hipGetLastError();
