@@ -421,9 +421,12 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 
     // Loads run one iteration ahead, into the registers just consumed: the
     // scales are used (and the next ones requested) first, then each plane
-    // word, replaced by the next iteration's as soon as it is extracted.  An
-    // iteration's first wait (for its scales) then covers only loads issued
-    // before the previous iteration's products.
+    // word, replaced by the next iteration's as soon as it is extracted.
+    // Every iteration issues the same 4 + 16 loads -- a plane that no slot
+    // of a step reads is requested out of range, which costs no memory
+    // access -- so the compiler's waits are exact: an iteration's first wait
+    // covers its scales and the loads before them, and each plane word's
+    // wait covers only that word and the loads issued before it.
     auto issue_scales = [&](int pb0, bool live, uint32_t (&sn)[4]) {
         const __amdgpu_buffer_rsrc_t rs = scale_rsrc(pb0, live);
 #pragma unroll
@@ -439,7 +442,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                if (s < tmax[u]) w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(r, voff(u, s), (int)(s * ldb8), 0);
+                w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(r, voff(u, s), (int)(s * ldb8), 0);
         issue_scales(pb0, true, sc);
     }
     for (; lb0 < lgend; lb0 += IB) {
@@ -490,21 +493,28 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
             }
         }
         issue_scales(pbn, more, sc);
-        // ---- codes to LDS (a step with no slot to read is skipped: its
-        // records meet zero coefficients)
+        // ---- codes to LDS (a step with no slot to read writes nothing: its
+        // stale records meet zero coefficients)
         if (more) mask_dead(pbn);
         const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pbn, more);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (tmax[u] == 0) continue;
+            // the step's depth as a fresh scalar each iteration, so its
+            // compares stay scalar branches instead of lane masks held (and
+            // spilled) across the loop
+            int tm = tmax[u];
+            asm volatile("" : "+s"(tm));
+            const bool act = tm != 0;  // wavefront-uniform
             v2i ch[4];
-            extract(w[u], tmax[u], ch);
+            if (act) extract(w[u], tm, ch);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                if (s < tmax[u]) w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(rn, voff(u, s), (int)(s * ldb8), 0);
+                w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(rn, voff(u, s), (int)(s * ldb8), 0);
+            if (act) {
 #pragma unroll
-            for (int rho = 0; rho < 4; ++rho)
-                *(v2i*)(code + wr[(rho + kSkewStep<C> * u) & 3] + u * 8 * C * kRec) = ch[rho];
+                for (int rho = 0; rho < 4; ++rho)
+                    *(v2i*)(code + wr[(rho + kSkewStep<C> * u) & 3] + u * 8 * C * kRec) = ch[rho];
+            }
         }
 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
