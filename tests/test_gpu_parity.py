@@ -360,6 +360,39 @@ def test_fused_fallback_when_the_sample_threshold_passes_too_few(F, orc):
     assert short == P * G  # every head needed the fallback
 
 
+def test_fused_threshold_keeps_candidate_lists_in_range(F, orc):
+    """On ordinary keys the sampled threshold (group-of-16 maxima of one run
+    in every s, estimated from the top digit rows) must leave between k and
+    the list capacity candidates for every head, so no head needs the full
+    rescan: a wrong sample stage would still give exact results through the
+    rescan, and only this check sees it.  The result must equal the
+    materialised path's (scores stored, then selected)."""
+    import torch
+
+    P, G, D, n, k, budget = 2, 4, 128, 524288 + 77, 256, 48
+    g = np.random.default_rng(4242)
+    x = [(g.standard_normal((n, D)) * np.exp(0.7 * g.standard_normal(D))).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, 4243)
+    s = _sample_stride(n, k)
+    assert n >= 128 * k * s and -(-2 * k // s) == 32  # group maxima; threshold at the 32nd
+    say("fused threshold range", n, k, s)
+    planes, scales = F.pack(dev(np.stack(x)))
+    pl = F.plan(dev(q), dev(s2), budget, 0)
+    out = F.TopkOut(P, G, n, k, pl.q_used.device, fused=True)
+    F.scan_topk_stage(1, planes, scales, n, pl, out)
+    F.scan_topk_stage(2, planes, scales, n, pl, out)
+    m = P * G
+    off = (m * 4 + 255) // 256 * 256  # candidate counts follow the thresholds
+    counts = out.ws[off:off + 4 * m].view(torch.int32).cpu().numpy()
+    cap = 8 * k * s + 1024
+    assert (counts >= k).all() and (counts <= cap).all(), counts
+    assert counts.mean() < 8 * k, counts  # about 2k expected
+    F.scan_topk_stage(3, planes, scales, n, pl, out)
+    ref = F.topk(F.scan(planes, scales, n, pl), n, k)
+    assert np.array_equal(out.idx.cpu().numpy(), ref.idx.cpu().numpy())
+    assert np.array_equal(out.union.cpu().numpy(), ref.union.cpu().numpy())
+
+
 def test_host_resident_index_matches_device(F, orc):
     """The scan reads a mapped pinned host copy of the index over the host
     link and must give the same bits as from HBM (KLT-rotated storage)."""
