@@ -52,7 +52,7 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kGroupBlocks = 256;                  // logical blocks per workgroup (at most)
+constexpr int kGroupBlocks = 1024;                 // logical blocks per workgroup (at most)
 constexpr int kRun = 32;                           // sampled blocks come in runs of 32
 constexpr int kSlotsMax = 128;
 constexpr int kRec = 32;                           // LDS bytes per (slot, half block) code record
@@ -741,8 +741,13 @@ hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
 {
     ScanArgs a = args;
     const int rows = a.list ? (P < kListRows ? P : kListRows) : P;
-    // blocks per workgroup: 256, or fewer (a multiple of every iteration's
-    // 16 blocks) when that leaves too few workgroups to fill the chip twice
+    // blocks per workgroup: 1024, or fewer (a multiple of every iteration's
+    // 16 blocks) when that leaves too few workgroups to fill the chip about
+    // three times.  Long ranges spread each workgroup's start-up (the pair's
+    // tables, the first loads, the last flush) over more blocks: at 1M
+    // tokens x 288 pairs the filtered scan takes 1.10 ms with 256 blocks per
+    // workgroup, 0.98 with 512, 0.96 with 1024 and 1.00 with 2048 (three
+    // rounds of workgroups instead of six).
     a.gb = kGroupBlocks;
     while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < 2048) a.gb /= 2;
     dim3 grid((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)rows);
