@@ -163,6 +163,9 @@ struct PairTables {
     float thr[4 * GR];                                      // FILTER: the heads' thresholds
     uint32_t qmax[4 * GR];
     uint32_t cnt[5];
+    float qv[4 * GR][kMaxD];                                // the heads' query values per channel
+    short act[kMaxD];                                       // the active list (first A entries)
+    unsigned char tch[kMaxD];                               // depth per channel
 };
 
 // wavefront max of a non-negative value, through DPP row operations
@@ -274,7 +277,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
             for (int x = 0; x < 2; ++x) {
                 const int h = 4 * gr + 2 * rhp + x;
                 qt[k][gr][x] = (e < A && h < G)
-                    ? __builtin_ldexpf(a.q_used[((size_t)p * G + h) * a.D + j], T.sig[h]) : 0.0f;
+                    ? __builtin_ldexpf(T.qv[h][j], T.sig[h]) : 0.0f;
             }
     }
     // constants column of read r: slots 32 r + 8 kap + 0..7
@@ -643,15 +646,26 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int A = a.n_active[p];
 
-    // ---- pair tables: slots sorted by depth (counting sort), scaled queries
+    // ---- pair tables: slots sorted by depth (counting sort), scaled queries.
+    // Every global value the tables need is requested at once (the active
+    // list, the channels' depths, the heads' query values, the thresholds),
+    // so a workgroup's set-up waits for one round trip to memory; the rest
+    // works in LDS.
+    uint32_t tk = 0;
+    if (MODE == kFilter && (int)threadIdx.x < G) tk = a.tau[(size_t)p * G + threadIdx.x];
+    for (int e = threadIdx.x; e < a.D; e += kThreads) {
+        T.act[e] = a.active[(size_t)p * a.D + e];  // entries past A are read but not used
+        T.tch[e] = (unsigned char)a.depth[(size_t)p * a.D + e];
+        for (int h = 0; h < G && h < NH; ++h) T.qv[h][e] = a.q_used[((size_t)p * G + h) * a.D + e];
+    }
     if (threadIdx.x < 5) T.cnt[threadIdx.x] = 0u;
     if (threadIdx.x < NH) T.qmax[threadIdx.x] = 0u;
     __syncthreads();
     for (int e = threadIdx.x; e < A; e += kThreads) {
-        const int j = a.active[(size_t)p * a.D + e];
-        atomicAdd(&T.cnt[a.depth[(size_t)p * a.D + j]], 1u);
+        const int j = T.act[e];
+        atomicAdd(&T.cnt[T.tch[j]], 1u);
         for (int h = 0; h < G && h < NH; ++h)  // |q| bits order like |q| values
-            atomicMax(&T.qmax[h], __float_as_uint(fabsf(a.q_used[((size_t)p * G + h) * a.D + j])));
+            atomicMax(&T.qmax[h], __float_as_uint(fabsf(T.qv[h][j])));
     }
     __syncthreads();
     if (threadIdx.x == 0) {  // start of each depth class, deepest first
@@ -673,10 +687,7 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
         }
         T.sig[threadIdx.x] = sg;
         float th = INFINITY;
-        if (MODE == kFilter && (int)threadIdx.x < G) {
-            const uint32_t tk = a.tau[(size_t)p * G + threadIdx.x];
-            th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
-        }
+        if (MODE == kFilter && (int)threadIdx.x < G) th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
         T.thr[threadIdx.x] = th;
     }
     __syncthreads();
@@ -685,8 +696,8 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
             const int e = e0 + lane;
             int j = 0, t = 0;
             if (e < A) {
-                j = a.active[(size_t)p * a.D + e];
-                t = a.depth[(size_t)p * a.D + j];
+                j = T.act[e];
+                t = T.tch[j];
             }
             for (int tt = 4; tt >= 1; --tt) {
                 const uint64_t m = __ballot(e < A && t == tt);
