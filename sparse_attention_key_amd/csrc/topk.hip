@@ -415,12 +415,6 @@ __device__ __forceinline__ int count_above(const T* a, int nch, T x)
     return r;
 }
 
-__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t cnt, uint32_t v)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < cnt) p[i] = v;
-}
-
 // The pairs with some head whose candidates overflowed their capacity, in
 // pair order: list[0] = how many, list[1..] = the pairs.  One workgroup.
 __global__ __launch_bounds__(kSelThreads) void overflow_list_kernel(const uint32_t* __restrict__ counts,
@@ -457,10 +451,12 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __r
                                                                 int64_t n, int64_t npad,
                                                                 int64_t stride, int64_t count,
                                                                 int64_t valid, int k,
-                                                                uint32_t* __restrict__ tau)
+                                                                uint32_t* __restrict__ tau,
+                                                                uint32_t* __restrict__ counts)
 {
     __shared__ SelShared sh;
     const int64_t m = blockIdx.x;
+    if (threadIdx.x == 0) counts[m] = 0u;  // the selection's candidate count, for the filter that follows
     if (valid < k) {
         if (threadIdx.x == 0) tau[m] = 0u;
         return;
@@ -760,10 +756,9 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
         valid += hi - lo;
     }
 
-    fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
     // (a sample of whole blocks' scores, 16x the fused path's: 1024 threads)
     threshold_kernel<<<dim3((unsigned)L.m), kSelThreads, 0, st>>>(scores, n, npad, L.stride,
-                                                              L.sample_nlb * 64, valid, k, tau);
+                                                              L.sample_nlb * 64, valid, k, tau, counts);
     {
         // chunks of 4096 scores on grid.y, looped inside once there are more
         // than enough workgroups to fill the chip (grid.y stays below 65536)
@@ -797,8 +792,8 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
     ScanArgs a = base;
 
     if (stages & 1) {
-        // threshold: scores of every stride-th block, exact k-th largest
-        fill_u32_kernel<<<dim3((unsigned)((L.m + 255) / 256)), 256, 0, st>>>(counts, L.m, 0u);
+        // threshold: scores of every stride-th block, exact k-th largest (the
+        // threshold kernel also clears the candidate counts)
         a.stride = L.stride;
         a.nlb = L.sample_nlb;
         a.out = sample;
@@ -808,7 +803,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         // of them is still a lower bound of the k-th largest score
         const int64_t row = L.sample_nlb * (L.lanemax ? 4 : 64);
         threshold_kernel<<<dim3((unsigned)L.m), kSelectThreads, 0, st>>>(sample, row, row, 1, row, row,
-                                                                     L.rank, tau);
+                                                                     L.rank, tau, counts);
     }
     if (stages & 2) {
         // filter: every block, keeping the scores at or above the threshold
