@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ s
 }
 
 // Eight waves per SIMD: two workgroups per CU.
-__global__ __launch_bounds__(kSelThreads, 8) void select_kernel(
+__global__ __launch_bounds__(kSelectThreads, 6) void select_kernel(
     const float* __restrict__ scores, int64_t n, int64_t npad, const uint32_t* __restrict__ counts,
     const uint64_t* __restrict__ cand, int64_t cap, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_val, int32_t* __restrict__ sorted_idx)
