@@ -625,8 +625,9 @@ __global__ __launch_bounds__(kSelectThreads, 6) void select_kernel(
 // element's place in the merged order is its own position plus the number
 // of elements of each other list that precede it (binary search; equal
 // indices ordered by list), then adjacent duplicates are dropped.
+template <int G>
 __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __restrict__ sorted_idx,
-                                                            int G, int k,
+                                                            int k,
                                                             int32_t* __restrict__ union_idx,
                                                             int32_t* __restrict__ union_len)
 {
@@ -652,14 +653,14 @@ __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __res
         if (e < total) {
             const int h = e / k;
             const int32_t x = a[e];
-            int cnt[kMaxG];
+            int cnt[G];
 #pragma unroll
-            for (int h2 = 0; h2 < kMaxG; ++h2) cnt[h2] = 0;
+            for (int h2 = 0; h2 < G; ++h2) cnt[h2] = 0;
             for (int st = top; st > 0; st >>= 1) {
 #pragma unroll
-                for (int h2 = 0; h2 < kMaxG; ++h2) {
+                for (int h2 = 0; h2 < G; ++h2) {
                     const int np = cnt[h2] + st;
-                    if (h2 < G && h2 != h && np <= k) {
+                    if (h2 != h && np <= k) {
                         const int32_t y = a[h2 * k + np - 1];
                         if (h2 < h ? y <= x : y < x) cnt[h2] = np;
                     }
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __res
             }
             int r = e - h * k;
 #pragma unroll
-            for (int h2 = 0; h2 < kMaxG; ++h2) r += (h2 < G && h2 != h) ? cnt[h2] : 0;
+            for (int h2 = 0; h2 < G; ++h2) r += h2 != h ? cnt[h2] : 0;
             val[u] = x;
             pos[u] = r;
         }
@@ -703,6 +704,24 @@ __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __res
         if (i == 0 || a[i] != a[i - 1]) out[q++] = a[i];
     for (int i = (int)all + threadIdx.x; i < total; i += blockDim.x) out[i] = -1;
     if (threadIdx.x == 0) union_len[p] = (int32_t)all;
+}
+
+// the union for G lists of k (the list count fixed at compile time, so the
+// searches over the other lists unroll without per-list tests)
+void launch_union(const int32_t* sorted, int P, int G, int k, int32_t* union_idx, int32_t* union_len,
+                  hipStream_t st)
+{
+    const dim3 grid((unsigned)P);
+    switch (G) {
+    case 1: union_kernel<1><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    case 2: union_kernel<2><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    case 3: union_kernel<3><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    case 4: union_kernel<4><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    case 5: union_kernel<5><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    case 6: union_kernel<6><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    case 7: union_kernel<7><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    default: union_kernel<8><<<grid, kSelThreads, 0, st>>>(sorted, k, union_idx, union_len); break;
+    }
 }
 
 }  // namespace
@@ -772,7 +791,7 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
     int32_t* sorted = (int32_t*)(w + L.off_sorted);
     select_kernel<<<dim3((unsigned)L.m), kSelectThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
                                                               k, topk_idx, topk_val, sorted);
-    union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(sorted, G, k, union_idx, union_len);
+    launch_union(sorted, P, G, k, union_idx, union_len, st);
     return hipGetLastError();
 }
 
@@ -830,7 +849,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         int32_t* sorted = (int32_t*)(w + L.off_sorted);
         select_kernel<<<dim3((unsigned)L.m), kSelectThreads, 0, st>>>(repair, n, npad, counts, cand,
                                                                   L.cap, k, topk_idx, topk_val, sorted);
-        union_kernel<<<dim3((unsigned)P), kSelThreads, 0, st>>>(sorted, G, k, union_idx, union_len);
+        launch_union(sorted, P, G, k, union_idx, union_len, st);
     }
     return hipGetLastError();
 }
