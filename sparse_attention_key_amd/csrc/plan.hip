@@ -26,11 +26,16 @@ __device__ __forceinline__ int depth_at(float w, float theta)
     return t;
 }
 
-// Sum of depths over the wavefront's channels at level theta.
-__device__ __noinline__ int total_depth(float w0, float w1, bool has0, bool has1, float theta)
+// Sum of depths over the wavefront's channels at level theta.  A lane's
+// share is 0..8, so the sum is assembled from one wavefront mask per bit
+// (four ballots and population counts instead of a shuffle chain).
+__device__ __forceinline__ int total_depth(float w0, float w1, bool has0, bool has1, float theta)
 {
-    int s = (has0 ? depth_at(w0, theta) : 0) + (has1 ? depth_at(w1, theta) : 0);
-    return wave_sum_i32(s);
+    const int s = (has0 ? depth_at(w0, theta) : 0) + (has1 ? depth_at(w1, theta) : 0);
+    int t = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) t += __popcll(__ballot((s >> b) & 1)) << b;
+    return t;
 }
 
 // Fixed r-channel plan: rank by group query energy, ties to the lower channel.
