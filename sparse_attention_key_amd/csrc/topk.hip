@@ -176,14 +176,18 @@ __device__ __forceinline__ uint32_t* level_begin(const Radix& r, SelShared& sh)
     return sh.hist[r.lvl & 1];
 }
 
+// Inclusive prefix sum over the wavefront with DPP moves: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes (lanes shifted in from outside the row
+// read 0), then row 0's total into row 1 and row 2's into row 3 (row_bcast
+// 15), then rows 0-1's total into rows 2 and 3 (row_bcast 31).
 __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
     return x;
 }
 
@@ -686,11 +690,7 @@ __global__ __launch_bounds__(kSelThreads) void union_kernel(const int32_t* __res
     for (int i = beg; i < beg + per && i < total; ++i)
         cnt += (i == 0 || a[i] != a[i - 1]) ? 1u : 0u;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    uint32_t x = cnt;
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_sum(cnt);
     if (lane == kWave - 1) wsum[wave] = x;
     __syncthreads();
     uint32_t off = 0, all = 0;
