@@ -38,6 +38,9 @@
  *  capacity of nb_cap >= nb blocks per row (L = nb_cap) and filled or
  *  extended with fathom_pack_range; calls that read it take nb_cap.
  *  Footprint: 68 bytes per token per pair at D = 128.
+ *  The scan entry points need one pair's plane rows to span less than 2^31
+ *  bytes (D * 32 * L < 2^31; at D = 128, L < 524,288 blocks or 33.5M tokens
+ *  per pair) and return FATHOM_ERR_UNSUPPORTED otherwise.
  */
 #ifndef FATHOM_H
 #define FATHOM_H
@@ -169,7 +172,8 @@ int fathom_plan(const float* q, const float* sigma2, const float* rot, int32_t P
  *       The result differs from the real dot product by at most
  *       15 (#read channels) 2^(E_b - 1 - sigma_h) + 2^-24 sum_j |q k| before
  *       the final rounding.  Padding tokens are -inf.
- * Errors: ERR_ARG (null), ERR_SHAPE, ERR_ALIGN.
+ * Errors: ERR_ARG (null), ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED (a pair's
+ * plane rows span 2^31 bytes or more).
  */
 int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D, int64_t n,
                 int64_t nb_cap, const uint8_t* depth, const int16_t* active,
@@ -178,7 +182,13 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32
 
 /*
  * fathom_topk -- the k best keys of every query head and their union per KV
- * head (the winner rows a step fetches).
+ * head (the winner rows a step fetches).  The byte-accounting section of the
+ * yeyulingfeng.com write-up ("先算一笔字节账") defines the selection: each
+ * query head keeps its k = 512 highest-scoring keys, and the G heads of a KV
+ * head fetch the union of their winners, at most G * k rows; its opening
+ * paragraph fixes that every key is scored before any is chosen.  Ties in
+ * score go to the lower token index and the union is listed in ascending
+ * order; the pages leave both open.
  *
  *   scores    [P][G][npad] from fathom_scan
  *   topk_idx  [P][G][k] int32 token indices ordered by (score descending,

@@ -21,6 +21,15 @@ inline int check_shape(int32_t P, int64_t n, int32_t D)
     return FATHOM_OK;
 }
 
+// The scan kernels address a pair's planes and scales with 32-bit buffer
+// offsets whose bit 31 marks a load as out of range, so a pair's plane rows
+// (D channels x 4 planes x L blocks x 8 bytes) must span less than 2^31 bytes:
+// at D = 128 that is L < 524,288 blocks, 33.5M tokens per pair.
+inline bool scan_offsets_fit(int32_t D, int64_t ldb)
+{
+    return (int64_t)D * 4 * ldb * 8 < ((int64_t)1 << 31);
+}
+
 // Row stride of the index in blocks: 0 selects ceil(n / 64); anything else
 // must hold the n tokens.  Returns -1 when invalid.
 inline int64_t row_blocks(int64_t n, int64_t nb_cap)
@@ -115,6 +124,7 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int32_t P, int32
     const int64_t ldb = row_blocks(n, nb_cap);
     if (ldb < 0) return FATHOM_ERR_SHAPE;
     if (G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
+    if (!scan_offsets_fit(D, ldb)) return FATHOM_ERR_UNSUPPORTED;
     const void* ps[] = {planes, scales, depth, active, n_active, q_used, scores};
     for (const void* p : ps)
         if (!aligned16(p)) return FATHOM_ERR_ALIGN;
@@ -167,6 +177,7 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
     const int64_t ldb = row_blocks(n, nb_cap);
     if (ldb < 0) return FATHOM_ERR_SHAPE;
     if (G < 1 || G > kMaxG) return FATHOM_ERR_SHAPE;
+    if (!scan_offsets_fit(D, ldb)) return FATHOM_ERR_UNSUPPORTED;
     if (k < 1 || k > n) return FATHOM_ERR_ARG;
     if (k > kMaxK || G * k > kMaxUnion) return FATHOM_ERR_UNSUPPORTED;
     const void* ps[] = {planes, scales, depth, active, n_active, q_used};

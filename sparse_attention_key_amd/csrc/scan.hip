@@ -191,7 +191,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int kap = lane >> 4, j16 = lane & 15;  // lane group (slot block / head) and row
-    // block indices fit 32 bits (the host checks the index size)
+    // block indices fit 32 bits (the host caps n below 2^31 tokens), and the
+    // plane and scale offsets below fit 31 bits (the host rejects a pair whose
+    // plane rows span 2^31 bytes or more)
     const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride;
     // Iteration i of wavefront w takes logical blocks lg0 + i IB + w NB + (0 .. NB-1):
     // at any time the four wavefronts of a workgroup read neighbouring blocks,

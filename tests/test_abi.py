@@ -76,6 +76,31 @@ def test_scan_validation(L):
     assert L.fathom_scan(*with_(0, MIS)) == F.ERR_ALIGN
 
 
+def test_scan_rejects_plane_spans_past_31_bit_offsets(L):
+    """A pair's plane rows (D x 4 x L words) must span less than 2^31 bytes,
+    the range of the scan's buffer offsets: at D = 128 that is L < 2^19."""
+    base = [A, A, 1, 128, 4096, 0, A, A, A, A, 4, A, None]
+
+    def scan(n, cap, D=128, planes=A):
+        b = list(base)
+        b[0], b[3], b[4], b[5] = planes, D, n, cap
+        return L.fathom_scan(*b)
+    # capacity index: 2^19 + 1 blocks per row, few tokens
+    assert scan(4096, (1 << 19) + 1) == F.ERR_UNSUPPORTED
+    assert scan(4096, 1 << 19) == F.ERR_UNSUPPORTED        # exactly 2^31 bytes
+    # dense index of 2^25 + 64 tokens: 2^19 + 1 blocks
+    assert scan((1 << 25) + 64, 0) == F.ERR_UNSUPPORTED
+    # the same row length at half the channels fits: the next check (a
+    # misaligned planes pointer) is the one that fails
+    assert scan((1 << 25) + 64, 0, D=64, planes=MIS) == F.ERR_ALIGN
+    assert scan(4096, (1 << 19) - 1, planes=MIS) == F.ERR_ALIGN
+    # fused path: the same check before the workspace is looked at
+    ws = L.fathom_scan_topk_workspace_bytes(1, 4, 4096, 64)
+    fused = [A, A, 1, 128, 4096, (1 << 19) + 1, A, A, A, A, 4, 64, A, None, A, A, A, ws, None]
+    assert L.fathom_scan_topk(*fused) == F.ERR_UNSUPPORTED
+    assert L.fathom_scan_topk_stage(2, *fused) == F.ERR_UNSUPPORTED
+
+
 def test_pack_range_validation(L):
     # keys, dtype, P, tok0, m, D, rot, planes, scales, nb_cap, stream
     base = [A, 0, 2, 128, 10, 128, None, A, A, 4, None]
