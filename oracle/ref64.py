@@ -9,6 +9,9 @@ forms used to pin the C oracle:
   (bit-plane section of the yeyulingfeng.com write-up);
 * ``requant_direct``   : the t-bit mid-rise quantiser applied to x directly;
 * ``scores_def``       : sum_j q_hj * k_ij in float64;
+* ``contract_bound``   : the error bound the scan's fixed-point score contract
+  states against ``scores_def``, and ``topk_valid``: whether a selection is
+  a top-k of the definition that this bound allows;
 * ``plan_bruteforce``  : exhaustive integer search of sum_j w_j 4^-t_j
   under sum_j t_j <= B (reverse water-filling section);
 * ``water_level_bisect``: the smallest theta by bisection on the fp32 bit
@@ -26,8 +29,11 @@ def f16_bits_to_f64(bits) -> np.ndarray:
     return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
 
 
-def decode_codes(planes: np.ndarray, n: int) -> np.ndarray:
-    """planes [D][4][nb] uint64 -> codes [D][n] (0..15)."""
+def decode_codes(planes: np.ndarray, n: int, channels=None) -> np.ndarray:
+    """planes [D][4][nb] uint64 -> codes [D][n] (0..15), or [len(channels)][n]
+    for the listed channels only."""
+    if channels is not None:
+        planes = planes[np.asarray(channels, np.int64)]
     D, S, nb = planes.shape
     bits = np.arange(64, dtype=np.uint64)
     codes = np.zeros((D, nb * 64), np.int64)
@@ -73,20 +79,73 @@ def pack_codes_def(keys: np.ndarray, scales_f64: np.ndarray) -> np.ndarray:
 
 def dequant_keys(planes, scales, n: int, depth) -> np.ndarray:
     """k_hat [D][n] in float64 for per-channel depths."""
-    codes = decode_codes(planes, n)
-    sc = f16_bits_to_f64(scales)[:, np.arange(n) // 64]
-    out = np.zeros(codes.shape, np.float64)
-    for j, t in enumerate(np.asarray(depth)):
-        t = int(t)
-        if t:
-            out[j] = dequant(prefix_code(codes[j], t), t, sc[j])
+    depth = np.asarray(depth)
+    read, kr = dequant_read(planes, scales, n, depth)
+    out = np.zeros((depth.shape[0], n), np.float64)
+    out[read] = kr
     return out
+
+
+def dequant_read(planes, scales, n: int, depth):
+    """(read channels, k_hat [#read][n] float64): the prefix keys of the
+    channels with depth > 0 only (what a scan reads)."""
+    depth = np.asarray(depth)
+    read = np.nonzero(depth)[0]
+    codes = decode_codes(planes, n, read)
+    sc = f16_bits_to_f64(np.asarray(scales)[read])[:, np.arange(n) // 64]
+    out = np.zeros(codes.shape, np.float64)
+    for r, j in enumerate(read):
+        t = int(depth[j])
+        out[r] = dequant(prefix_code(codes[r], t), t, sc[r])
+    return read, out
 
 
 def scores_def(planes, scales, n: int, depth, q_used) -> np.ndarray:
     """[G][n] float64: sum over channels of q_hj * k_hat_ij."""
-    kh = dequant_keys(planes, scales, n, depth)
-    return np.asarray(q_used, np.float64) @ kh
+    read, kr = dequant_read(planes, scales, n, depth)
+    return np.asarray(q_used, np.float64)[:, read] @ kr
+
+
+def contract_bound(planes, scales, n: int, depth, q_used, s_def=None) -> np.ndarray:
+    """[G][n] bound on |score - s_def| that the fixed-point score contract of
+    the scan states: before its final rounding a score differs from the real
+    dot product by at most 15 (#read channels) 2^(E_b - 1 - sigma_h) (the
+    truncated coefficients times codes of magnitude <= 15) plus
+    2^-24 sum_j |q_hj k_ij| (one float32 product per coefficient); the final
+    rounding to float32 adds at most 2^-24 of the magnitude.  sigma_h =
+    31 - floor(log2 max_j |q_hj|) over the read channels (0 when all are 0);
+    E_b = (the largest binary16 exponent field of the read channels' scales
+    in block b, at least 1) - 15."""
+    depth = np.asarray(depth)
+    q = np.asarray(q_used, np.float64)
+    read, kr = dequant_read(planes, scales, n, depth)
+    if s_def is None:
+        s_def = q[:, read] @ kr
+    if read.size == 0:
+        return np.zeros((q.shape[0], n))
+    qmax = np.abs(q[:, read]).max(1)
+    sigma = np.where(qmax > 0, 31 - np.floor(np.log2(np.where(qmax > 0, qmax, 1.0))), 0.0)
+    ef = np.maximum(1, (np.asarray(scales)[read].astype(np.int64) >> 10) & 31).max(0)  # [nb]
+    unit = np.exp2((ef - 15).astype(np.float64)[np.arange(n) // 64][None, :] - 1 - sigma[:, None])
+    pre = 15 * read.size * unit + 2.0 ** -24 * (np.abs(q[:, read]) @ np.abs(kr))
+    return pre + 2.0 ** -24 * (np.abs(s_def) + pre) + 2.0 ** -149
+
+
+def topk_valid(s_def_row, bound_row, idx, n: int) -> bool:
+    """Whether idx (k distinct tokens < n) is a valid top-k of scores known
+    only to within +-bound of s_def: no token left out may be certainly above
+    a token taken, i.e. min over winners of (s_def + bound) >= max over the
+    others of (s_def - bound)."""
+    idx = np.asarray(idx, np.int64)
+    if idx.size == 0 or np.unique(idx).size != idx.size or idx.min() < 0 or idx.max() >= n:
+        return False
+    s = np.asarray(s_def_row[:n], np.float64)
+    b = np.asarray(bound_row[:n], np.float64)
+    taken = np.zeros(n, bool)
+    taken[idx] = True
+    if taken.all():
+        return True
+    return bool((s[taken] + b[taken]).min() >= (s[~taken] - b[~taken]).max())
 
 
 def objective(w, t) -> float:

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import need_gpu, say, u16, u64
+from tests.gpu_util import assert_selection_valid, need_gpu, say, u16, u64
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +94,8 @@ def _compare_sampled(orc, w, sample, q, s2, budget, mode, planes, scales, pl, sc
         assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"])
         assert int(out.union_len[p]) == ref["union_len"]
         assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+        say("selection against the float64 definition, pair", p)
+        assert_selection_valid(orc, rp, rs, w.n, ref["depth"], ref["q_used"], out.idx[p].cpu().numpy())
 
 
 @pytest.fixture(scope="module")

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import bf16_dev, dev, need_gpu, say, score_tol, u16, u64
+from tests.gpu_util import assert_selection_valid, bf16_dev, dev, need_gpu, say, score_tol, u16, u64
 
 pytestmark = pytest.mark.gpu
 
@@ -224,6 +224,7 @@ def _compare_pair(orc, p, x, q, s2, budget, k, n, pl, scores, out, mode=0, rot=N
     assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"])
     assert out.union_len[p].item() == ref["union_len"]
     assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+    assert_selection_valid(orc, rp, rs, n, ref["depth"], ref["q_used"], out.idx[p].cpu().numpy())
     return rp, rs
 
 
@@ -304,6 +305,7 @@ def test_fused_scan_topk_bit_exact(F, orc, kind, n, D, G, budget, k, mode):
             assert np.array_equal(val[p, h], ref["scores"][h][ref["topk"][h]])
         assert int(out.union_len[p]) == ref["union_len"]
         assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+        assert_selection_valid(orc, rp, rs, n, ref["depth"], ref["q_used"], idx[p])
 
 
 def _sample_stride(n, k):

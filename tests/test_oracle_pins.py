@@ -338,19 +338,9 @@ def test_single_channel_single_plane_by_hand(orc):
 
 
 def _def_and_bound(orc, planes, scales, n, depth, q):
-    """float64 definition and the contract's stated error bound before the
-    final rounding: 15 * (#read channels) * 2^(E_b - 1 - sigma_h) per block
-    plus 2^-24 * sum_j |q_hj k_ij|."""
+    """float64 definition and the contract's stated error bound."""
     ref = orc.ref64.scores_def(planes, scales, n, depth, q)
-    k = orc.ref64.dequant_keys(planes, scales, n, depth)  # [D][n] prefix keys
-    read = np.nonzero(depth)[0]
-    qmax = np.abs(q[:, read]).max(1)
-    sigma = np.where(qmax > 0, 31 - np.floor(np.log2(np.where(qmax > 0, qmax, 1))), 0)
-    ef = np.maximum(1, (scales[read] >> 10) & 31).max(0)  # [nb]
-    E = ef.astype(np.float64) - 15
-    unit = np.exp2(E[np.arange(n) // 64][None, :] - 1 - sigma[:, None])
-    bound = 15 * read.size * unit + 2.0 ** -24 * (np.abs(q[:, read, None]) * np.abs(k[read][None, :, :])).sum(1)
-    return ref, bound
+    return ref, orc.ref64.contract_bound(planes, scales, n, depth, q, s_def=ref)
 
 
 def test_fixed_point_scores_within_their_bound(orc):
@@ -365,7 +355,7 @@ def test_fixed_point_scores_within_their_bound(orc):
         depth, _, qu = orc.plan(q, s2, B)
         s = orc.scores(planes, scales, n, depth, qu)[:, :n].astype(np.float64)
         ref, bound = _def_and_bound(orc, planes, scales, n, depth, qu)
-        assert np.all(np.abs(s - ref) <= bound + np.abs(ref) * 2.0 ** -24)
+        assert np.all(np.abs(s - ref) <= bound)
 
 
 def test_fixed_point_exact_when_representable(orc):
@@ -412,6 +402,62 @@ def test_scores_within_tolerance_of_definition(orc):
     smax = orc.ref64.f16_bits_to_f64(scales).max()
     tol = 1e-5 * np.abs(ref) + 1e-6 * np.abs(qu).sum(1, keepdims=True) * smax
     assert np.all(np.abs(s32 - ref) <= tol)
+
+
+def _selection_cases(orc):
+    """(planes, scales, n, q, s2, budget, k) cases: random keys with wide
+    channel scales at several budgets and k, and the tiny workload."""
+    import workloads as wl
+
+    cases = []
+    for seed, n, B, k in ((60, 3000, 48, 64), (61, 3000, 7, 512), (62, 2500, 136, 1), (63, 4097, 512, 300),
+                          (64, 3000, 32, 64)):
+        x, planes, scales, q = _rand_index(orc, n, seed)
+        s2 = np.exp(np.random.default_rng(seed + 1).standard_normal(128)).astype(np.float32)
+        cases.append((planes, scales, n, q, s2, B, k))
+    w = wl.WORKLOADS["tiny"]
+    planes, scales = orc.pack(wl.keys_host(w, 0))
+    s2 = orc.calib.channel_variance(wl.calibration_sample(w, 0))
+    cases.append((planes, scales, w.n, wl.queries(w, 0), s2, w.budget, w.k))
+    return cases
+
+
+def test_contract_topk_is_a_valid_topk_of_the_definition(orc):
+    # The selected sets are exact under the fixed-point contract; against the
+    # plain float64 definition (the query times the prefix-dequantised keys)
+    # they must be a top-k that the contract's stated error bound allows, and
+    # exactly the definition's top-k wherever its k-th and (k+1)-th scores
+    # are further apart than the bounds.
+    forced = 0
+    for planes, scales, n, q, s2, B, k in _selection_cases(orc):
+        ref = orc.step(planes, scales, n, q, s2, B, k)
+        s_def = orc.ref64.scores_def(planes, scales, n, ref["depth"], ref["q_used"])
+        bnd = orc.ref64.contract_bound(planes, scales, n, ref["depth"], ref["q_used"], s_def=s_def)
+        for h in range(q.shape[0]):
+            assert orc.ref64.topk_valid(s_def[h], bnd[h], ref["topk"][h], n)
+            order = orc.ref64.topk_def(s_def[h], n, n)
+            win, rest = order[:k], order[k:]
+            if rest.size == 0 or (s_def[h, win] - bnd[h, win]).min() > (s_def[h, rest] + bnd[h, rest]).max():
+                forced += 1
+                assert set(ref["topk"][h].tolist()) == set(win.tolist())
+    assert forced >= 6  # the margin case is exercised, not only the band
+
+
+def test_topk_validity_check_rejects_a_wrong_selection(orc):
+    # the check has teeth: trading the weakest winner for the strongest loser
+    # (far apart here) or repeating a token is not a valid top-k
+    planes, scales, n, q, s2, B, k = _selection_cases(orc)[0]
+    ref = orc.step(planes, scales, n, q, s2, B, k)
+    s_def = orc.ref64.scores_def(planes, scales, n, ref["depth"], ref["q_used"])
+    bnd = orc.ref64.contract_bound(planes, scales, n, ref["depth"], ref["q_used"], s_def=s_def)
+    order = orc.ref64.topk_def(s_def[0], n, n)
+    bad = order[:k].copy()
+    bad[-1] = order[-1]  # the lowest-scoring token instead of the k-th
+    assert not orc.ref64.topk_valid(s_def[0], bnd[0], bad, n)
+    dup = order[:k].copy()
+    dup[-1] = dup[0]
+    assert not orc.ref64.topk_valid(s_def[0], bnd[0], dup, n)
+    assert orc.ref64.topk_valid(s_def[0], bnd[0], order[:k], n)
 
 
 # ------------------------------------------------------------------ top-k
