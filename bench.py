@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--mode", type=int, default=0, help="0 water-filling, 1 fixed top-r, 2 uniform")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle beside it")
     ap.add_argument("--cpu-pairs", type=int, default=32)
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the all-cores leg (0: the CPUs this process may use, at most 16)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -293,11 +294,31 @@ def append_probe(F, w, planes, scales, device):
     return {"pairs": w.P, "tokens_in_block": m, "us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2)}
 
 
-def cpu_baseline(w, q, budget, mode, pairs, threads):
+def cpu_info() -> dict:
+    """Host CPU facts for the baseline line: model string, online CPUs, and
+    the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": affinity}
+
+
+def cpu_baseline(w, q, budget, mode, pairs, threads, single_pairs=2):
     """Time the CPU oracle (as it stands) on a bounded sample of pairs: the
-    same plan + scores + top-k + union per pair, run `threads` pairs at a
-    time; scaled to a whole step of all pairs.  Its calibration statistics
-    come from the oracle, on the same calibration samples."""
+    same plan + scores + top-k + union per pair.  Two legs: one pair after
+    another on one thread, and the sample spread over `threads` host threads
+    (one pair per thread at a time).  Both are scaled to a whole step of all
+    pairs.  The oracle's calibration statistics come from the oracle, on the
+    same calibration samples."""
     import oracle
     import workloads as wl
 
@@ -336,14 +357,27 @@ def cpu_baseline(w, q, budget, mode, pairs, threads):
         oracle.step(pl, sc, w.n, q[p], s2[p], budget, w.k, mode=mode,
                     rot=None if rot is None else rot[p])
 
+    single = sel[:single_pairs]
+    t0 = time.perf_counter()
+    for p in single:
+        run(p)
+    wall1 = time.perf_counter() - t0
+    ms1 = wall1 * 1e3 * w.P / len(single)
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(run, sel))
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 * w.P / pairs
-    return {"value": round(ms_step, 3), "unit": "ms/step", "cores": min(threads, pairs), "kind": "oracle",
-            "sample": f"{pairs} of {w.P} pairs at n={w.n} (plan+fixed-point scores+top-k+union per pair, "
-                      f"{min(threads, pairs)} pairs in parallel, {wall:.1f}s wall), scaled x{w.P / pairs:.1f}"}
+    used = min(threads, pairs)
+    info = cpu_info()
+    log(f"cpu baseline: {ms1:.0f} ms/step on one thread, {ms_step:.0f} ms/step on {used} threads; {info}")
+    return {"value": round(ms_step, 3), "unit": "ms/step", "cores": used, "kind": "oracle",
+            "sample": f"{pairs} of {w.P} pairs at n={w.n} (plan+fixed-point scores+top-k+union per pair), "
+                      f"{used} pairs at a time on {used} host threads ({wall:.1f}s wall), scaled x{w.P / pairs:.1f}",
+            "single_thread": {"value": round(ms1, 3), "unit": "ms/step", "cores": 1,
+                              "sample": f"{len(single)} pairs one after another ({wall1:.1f}s), "
+                                        f"scaled x{w.P / len(single):.1f}"},
+            **info}
 
 
 def main():
@@ -489,7 +523,8 @@ def main():
         res["append"] = append_probe(F, w, planes, scales, dev)
         log(f"append (repack the last block of every pair): {res['append']}")
     if a.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, q_np, budget, a.mode, a.cpu_pairs, a.cpu_threads)
+        threads = a.cpu_threads or min(16, cpu_info()["affinity_cpus"])
+        res["cpu_baseline"] = cpu_baseline(w, q_np, budget, a.mode, a.cpu_pairs, threads)
     print(json.dumps(res), flush=True)
 
 
