@@ -84,12 +84,18 @@ def _check(fn: str, rc: int):
 
 
 def _ptr(t):
-    """Device address of a tensor, or a raw address given as an int (e.g. a
-    mapped pinned host buffer)."""
+    """Device address of a dense device tensor, or a raw address given as an
+    int (e.g. a mapped pinned host buffer).  Strided or host tensors are
+    refused: the library reads every array as dense row-major memory."""
     if t is None:
         return None
     if isinstance(t, int):
         return ctypes.c_void_p(t)
+    if not t.is_cuda:
+        raise ValueError("fathom: tensor arguments must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"fathom: tensor of shape {tuple(t.shape)} is not contiguous; "
+                         "the entry points read dense row-major arrays")
     return ctypes.c_void_p(t.data_ptr())
 
 

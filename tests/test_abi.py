@@ -177,3 +177,14 @@ def test_calib_validation(L):
     assert L.fathom_calib_basis(A, 2, 129, A, A, None) == F.ERR_SHAPE
     assert L.fathom_calib_basis(A, 0, 128, A, A, None) == F.ERR_SHAPE
     assert L.fathom_calib_basis(MIS, 2, 128, A, A, None) == F.ERR_ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    """The binding hands the library raw addresses; a host tensor has none
+    the GPU can read, so it is refused before any call."""
+    import torch
+
+    with pytest.raises(ValueError, match="device memory"):
+        F._ptr(torch.zeros(4))
+    assert F._ptr(None) is None
+    assert F._ptr(4096).value == 4096

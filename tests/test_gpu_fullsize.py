@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import assert_selection_valid, need_gpu, say, u16, u64
+from tests.gpu_util import assert_selection_valid, dev, need_gpu, say, u16, u64
 
 pytestmark = pytest.mark.gpu
 
@@ -144,4 +144,66 @@ def test_long1m_step(F, orc):
     del fused
     _compare_sampled(orc, w, [3, 150, 286], q, s2, w.budget, 0, planes, scales, pl, scores, out)
     del planes, scales, scores, out
+    torch.cuda.empty_cache()
+
+
+def test_host1m_klt_sampled_pairs(F, orc):
+    """The host-resident, KLT-rotated workload at its full length: four of
+    the 288 pairs, 1,048,576 tokens each, packed in the calibration basis
+    and read by the fused scan from mapped pinned host memory over the host
+    link.  Planes, plan, scores of every token, top-k and union are compared
+    bit for bit with the oracle on the same stored coordinates, and the
+    selections against the float64 score definition."""
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    w = wl.WORKLOADS["host1m_klt"]
+    pairs = [0, 97, 190, 287]
+    P, n = len(pairs), w.n
+    q = np.stack([wl.queries(w, p) for p in pairs])
+    rots, lams = zip(*[orc.calib.klt_basis(wl.calibration_sample(w, p)) for p in pairs])
+    rot, lam = np.stack(rots), np.stack(lams)
+    say("host1m_klt: keys of 4 pairs in the calibration basis")
+    keys = wl.keys_device(w, pairs)
+    y = torch.empty((P, n, w.D), dtype=torch.float32, device="cuda")
+    for i in range(P):  # stored coordinates: the same float32 values for both sides
+        y[i] = keys[i].float() @ torch.from_numpy(rot[i]).cuda()
+    del keys
+    planes = torch.empty((P, w.D, 4, w.nb), dtype=torch.int64, device="cuda")
+    scales = torch.empty((P, w.D, w.nb), dtype=torch.int16, device="cuda")
+    F.pack_into(y, planes, scales)
+    y_host = y.cpu().numpy()
+    del y
+    ph = PinnedHost(planes.numel() * 8)
+    sh = PinnedHost(scales.numel() * 2)
+    st = torch.cuda.current_stream()
+    ph.copy_from_device(0, planes.data_ptr(), planes.numel() * 8, st)
+    sh.copy_from_device(0, scales.data_ptr(), scales.numel() * 2, st)
+    torch.cuda.synchronize()
+    say("host1m_klt: fused scan + top-k over the host link")
+    pl = F.plan(torch.from_numpy(q).cuda(), torch.from_numpy(lam).cuda(), w.budget, 0,
+                rot=dev(rot))
+    out = F.scan_topk(ph.dev, sh.dev, n, pl, w.k)
+    s_host = F.scan(ph.dev, sh.dev, n, pl)
+    torch.cuda.synchronize()
+
+    def oracle_pair(i):
+        rp, rs = orc.pack(y_host[i])
+        return i, rp, rs, orc.step(rp, rs, n, q[i], lam[i], w.budget, w.k, rot=rot[i])
+
+    with cf.ThreadPoolExecutor(max_workers=P) as ex:
+        refs = list(ex.map(oracle_pair, range(P)))
+    for i, rp, rs, ref in refs:
+        say("host1m_klt: compare pair", pairs[i])
+        assert np.array_equal(u64(planes[i]), rp)
+        assert np.array_equal(u16(scales[i]), rs)
+        assert np.array_equal(pl.depth[i].cpu().numpy(), ref["depth"])
+        assert np.array_equal(pl.q_used[i].cpu().numpy().view(np.uint32), ref["q_used"].view(np.uint32))
+        assert np.array_equal(s_host[i].cpu().numpy().view(np.uint32), ref["scores"].view(np.uint32))
+        assert np.array_equal(out.idx[i].cpu().numpy(), ref["topk"])
+        assert int(out.union_len[i]) == ref["union_len"]
+        assert np.array_equal(out.union[i].cpu().numpy(), ref["union"])
+        assert_selection_valid(orc, rp, rs, n, ref["depth"], ref["q_used"], out.idx[i].cpu().numpy())
+    ph.free()
+    sh.free()
+    del planes, scales, s_host, out
     torch.cuda.empty_cache()

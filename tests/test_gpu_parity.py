@@ -542,3 +542,19 @@ def test_scan_topk_on_capacity_index(F, orc):
         ref = orc.step(rp, rs, n, q[p], s2[p], budget, k)
         assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"]), p
         assert np.array_equal(out.union[p].cpu().numpy(), ref["union"]), p
+
+
+def test_binding_refuses_strided_tensors(F):
+    """A transposed view has the right shape but not the row-major layout
+    the entry points read: the binding refuses it instead of passing its
+    storage through (a transposed rotation would silently give another
+    plan)."""
+    import torch
+
+    rot = torch.eye(64, device="cuda") + torch.arange(4096, device="cuda").reshape(64, 64) / 4096
+    q = torch.ones((1, 2, 64), device="cuda")
+    s2 = torch.ones((1, 64), device="cuda")
+    with pytest.raises(ValueError, match="not contiguous"):
+        F.plan(q, s2, 16, 0, rot=rot.t().unsqueeze(0))
+    F.plan(q, s2, 16, 0, rot=rot.t().contiguous().unsqueeze(0))
+
