@@ -219,11 +219,12 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
  * candidates, and the k best candidates are selected exactly.  A head that
  * ends up with fewer than k candidates (the sample misjudged it) or more
  * than their capacity (massive ties) has its pair rescanned into a full
- * score buffer inside the workspace and is selected from there; results are
- * exact either way.
- *   ws  device workspace of at least fathom_scan_topk_workspace_bytes(); it
- *       includes that fallback buffer (P * G * npad floats), which is only
- *       written when a capacity is exceeded.
+ * score row inside the workspace and is selected from there; results are
+ * exact either way.  The rows are min(P, 16) pairs' worth (G * npad floats
+ * each): one workgroup per row rescans the failed pairs in turn, so the
+ * workspace does not grow with the number of failures (at 1M tokens x 288
+ * pairs, G = 4, k = 512 it is about 0.9 GB).
+ *   ws  device workspace of at least fathom_scan_topk_workspace_bytes().
  * Errors: as fathom_scan and fathom_topk.
  */
 size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k);

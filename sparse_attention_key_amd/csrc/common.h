@@ -131,10 +131,8 @@ struct ScanArgs {
     uint32_t* counts;      // FILTER: [P][G]
     uint64_t* cand;        // FILTER: [P][G][cap]
     int64_t cap;
-    const uint32_t* list;  // optional (score mode): list[0] pairs listed in list[1..]; only they are scanned
     int gb;                // logical blocks per workgroup (set by the launcher)
 };
-constexpr int kListRows = 4;  // workgroup rows that walk a pair list
 // mode: 0 store scores, 1 filter into candidates, 2 per-lane maxima
 hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream_t st);
 
@@ -156,12 +154,23 @@ struct TopkLayout {
     bool lanemax;        // fused threshold from per-lane maxima of the sample
     int rank;            // fused threshold: this order statistic of the sample
     size_t off_tau, off_count, off_cand, off_sorted, bytes;  // top-k from given scores
-    size_t off_list, off_sample, off_repair, bytes_fused;  // fused scan + top-k
+    int slots;           // fused: full score rows (pairs) for the repair, reused in turn
+    size_t off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };
+// Repair rows of the fused path: a workgroup per row rescans one failed pair
+// at a time, so this bounds both the workspace and the repair's parallelism.
+constexpr int kRepairSlots = 16;
 TopkLayout topk_layout(int P, int G, int64_t n, int k);
 hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,
                        float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
                        const TopkLayout& L, hipStream_t st);
+// Selections whose candidate count c fails (c > cap or c < k): each of
+// `slots` workgroups rescans failed pairs in turn into its own row of
+// G x npad scores (rows: [slots][G][npad] floats) and selects the failed
+// heads there exactly.
+hipError_t launch_repair(const ScanArgs& base, int P, int G, int k, const uint32_t* counts, int64_t cap,
+                         float* rows, int slots, int32_t* topk_idx, float* topk_val, int32_t* sorted_idx,
+                         hipStream_t st);
 hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* topk_idx,
                             float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
                             const TopkLayout& L, int stages, hipStream_t st);

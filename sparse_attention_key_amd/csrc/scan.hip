@@ -41,7 +41,7 @@
 // integer bound on the top digits screens the tokens, survivors get their
 // exact score); LANEMAX writes, per block and head, the maxima of four
 // groups of 16 tokens (the input of the top-k threshold).
-#include "common.h"
+#include "select.h"
 
 namespace fathom {
 namespace {
@@ -180,10 +180,13 @@ __device__ __forceinline__ int wave_max_dpp(int v)
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Tile `tile` of pair p: logical blocks tile * gb .. tile * gb + gb - 1.
+// STORE and LANEMAX write row `op` of the output (the pair itself, or a
+// repair row).
 template <int GR, int MODE, int C>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const int G, const int A,
-                                          const PairTables<GR>& T, unsigned char* code,
-                                          unsigned char* coef, v4i* stage)
+                                          const int tile, const int op, const PairTables<GR>& T,
+                                          unsigned char* code, unsigned char* coef, v4i* stage)
 {
     constexpr int S = 32 * C, NB = 4 / C;
     constexpr int NH = 4 * GR;
@@ -198,7 +201,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     // Iteration i of wavefront w takes logical blocks lg0 + i IB + w NB + (0 .. NB-1):
     // at any time the four wavefronts of a workgroup read neighbouring blocks,
     // so each 128-byte line of a plane row is used by all of them at once.
-    const int lg0 = (int)blockIdx.x * a.gb;
+    const int lg0 = tile * a.gb;
     const int lgend = min(lg0 + a.gb, nlb);
     if (lg0 + wave * NB >= lgend) return;
     const int64_t ldb = a.ldb;
@@ -598,7 +601,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                             const int h = kap + 4 * gr;
                             const float sc = exact_score(o[rho][gr], recombine(kk[gr]), rho, Eb[b] - 1 - sig[gr]);
                             if (h < G && lb < nlb)
-                                a.out[((size_t)p * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
+                                a.out[((size_t)op * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
                                     tval ? sc : -INFINITY;
                         }
                     }
@@ -626,7 +629,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                                          0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
                         const int h = kap + 4 * gr;
                         if ((j16 & 3) == 0 && h < G && lb < nlb)
-                            a.out[((size_t)p * G + h) * (a.nlb * 4) + (int64_t)lb * 4 + (j16 >> 2)] = v;
+                            a.out[((size_t)op * G + h) * (a.nlb * 4) + (int64_t)lb * 4 + (j16 >> 2)] = v;
                     }
                 }
             }
@@ -637,7 +640,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 }
 
 template <int GR, int MODE>
-__device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const int G)
+__device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const int G, const int tile,
+                                          const int op)
 {
     constexpr int NH = 4 * GR;
     __shared__ PairTables<GR> T;
@@ -728,41 +732,95 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
     unsigned char* code = s_code[wave];
     unsigned char* coef = s_coef[wave];
     v4i* stage = s_stage[MODE == kFilter ? wave : 0];
-    if (A <= 32) scan_body<GR, MODE, 1>(a, p, G, A, T, code, coef, stage);
-    else if (A <= 64) scan_body<GR, MODE, 2>(a, p, G, A, T, code, coef, stage);
-    else scan_body<GR, MODE, 4>(a, p, G, A, T, code, coef, stage);
+    if (A <= 32) scan_body<GR, MODE, 1>(a, p, G, A, tile, op, T, code, coef, stage);
+    else if (A <= 64) scan_body<GR, MODE, 2>(a, p, G, A, tile, op, T, code, coef, stage);
+    else scan_body<GR, MODE, 4>(a, p, G, A, tile, op, T, code, coef, stage);
 }
 
-// blockIdx.y is the pair; with a pair list (score mode only), the rows of
-// the grid take the listed pairs in turn instead.
+// blockIdx.y is the pair, blockIdx.x its tile of gb logical blocks.
 template <int GR, int MODE>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a, int G)
 {
-    if (MODE == kStore && a.list) {
-        const uint32_t nlist = a.list[0];
-        for (uint32_t r = blockIdx.y; r < nlist; r += gridDim.y) {
-            scan_pair<GR, MODE>(a, (int)a.list[1 + r], G);
-            __syncthreads();  // the pair's LDS tables are rewritten by the next one
+    scan_pair<GR, MODE>(a, (int)blockIdx.y, G, (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// Fused path, stage 3: exact selection of the heads whose candidate list
+// failed (more than cap candidates, or fewer than k).  The failed pairs are
+// numbered in pair order; workgroup w takes those numbered w, w + slots, ...
+// in turn, rescans each whole pair (one tile of every block) into its own
+// row of G x npad scores and selects each failed head over that row, so the
+// workspace holds `slots` rows whatever the number of failures.
+template <int GR>
+__global__ __launch_bounds__(kThreads) void repair_kernel(ScanArgs a, int P, int G, int k,
+                                                          const uint32_t* __restrict__ counts, int64_t cap,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_val,
+                                                          int32_t* __restrict__ sorted_idx)
+{
+    __shared__ SelShared sh;
+    __shared__ int s_fail[kThreads];
+    __shared__ uint32_t s_wsum[kWaves];
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int64_t npad = a.nlb * 64;
+    float* row = a.out + (size_t)blockIdx.x * G * npad;
+    auto failed = [&](int64_t m) {
+        const int64_t c = counts[m];
+        return c > cap || c < (int64_t)k;
+    };
+    uint32_t seen = 0;  // failed pairs before this chunk
+    for (int p0 = 0; p0 < P; p0 += kThreads) {
+        const int p = p0 + (int)threadIdx.x;
+        bool f = false;
+        if (p < P)
+            for (int h = 0; h < G; ++h) f |= failed((int64_t)p * G + h);
+        const uint64_t b = __ballot(f);
+        if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(b);
+        __syncthreads();
+        uint32_t off = 0, nf = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            off += w < wave ? s_wsum[w] : 0u;
+            nf += s_wsum[w];
         }
-        return;
+        if (f) s_fail[off + (uint32_t)__popcll(b & lanes_below(lane))] = p;
+        __syncthreads();
+        for (uint32_t i = 0; i < nf; ++i) {
+            if ((seen + i) % gridDim.x != blockIdx.x) continue;
+            const int fp = s_fail[i];
+            scan_pair<GR, kStore>(a, fp, G, 0, (int)blockIdx.x);
+            __syncthreads();  // the row is complete (and the pair's LDS tables free)
+            for (int h = 0; h < G; ++h) {
+                const int64_t m = (int64_t)fp * G + h;
+                if (!failed(m)) continue;
+                select_one(row + (size_t)h * npad, a.n, npad, true, nullptr, 0, k, m, topk_idx, topk_val,
+                           sorted_idx, sh);
+                __syncthreads();  // sh is reused by the next head
+            }
+        }
+        seen += nf;
+        __syncthreads();  // s_fail and s_wsum are rewritten by the next chunk
     }
-    scan_pair<GR, MODE>(a, (int)blockIdx.y, G);
 }
 
 template <int MODE>
 hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
 {
     ScanArgs a = args;
-    const int rows = a.list ? (P < kListRows ? P : kListRows) : P;
+    const int rows = P;
     // blocks per workgroup: 1024, or fewer (a multiple of every iteration's
-    // 16 blocks) when that leaves too few workgroups to fill the chip about
-    // three times.  Long ranges spread each workgroup's start-up (the pair's
+    // 16 blocks, at least 64) while the grid has fewer workgroups than
+    // `target`.  Long ranges spread each workgroup's start-up (the pair's
     // tables, the first loads, the last flush) over more blocks: at 1M
     // tokens x 288 pairs the filtered scan takes 1.10 ms with 256 blocks per
-    // workgroup, 0.98 with 512, 0.96 with 1024 and 1.00 with 2048 (three
-    // rounds of workgroups instead of six).
+    // workgroup, 0.98 with 512, 0.96 with 1024 and 1.00 with 2048.  For the full
+    // scans (filter, scores) a grid of about two workgroups per CU is best
+    // when the pairs are few: at 1M tokens x 8 pairs (one layer) the filter
+    // takes 110 us with 2048 workgroups of 64 blocks, 77 with 1024, 56 with
+    // 512 and 64 with 256.  The sampled stage reads one
+    // run in 16, so its workgroups are short and more of them (2048) keep the
+    // chip busy: 0.105 ms at 288 pairs against 0.125 with 512.
+    const int64_t target = MODE == kLaneMax ? 2048 : 512;
     a.gb = kGroupBlocks;
-    while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < 2048) a.gb /= 2;
+    while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < target) a.gb /= 2;
     dim3 grid((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)rows);
     if (G <= 4) scan_kernel<1, MODE><<<grid, kThreads, 0, st>>>(a, G);
     else scan_kernel<2, MODE><<<grid, kThreads, 0, st>>>(a, G);
@@ -776,6 +834,21 @@ hipError_t launch_scan_args(const ScanArgs& a, int P, int G, int mode, hipStream
     if (mode == kFilter) return launch_mode<kFilter>(a, P, G, st);
     if (mode == kLaneMax) return launch_mode<kLaneMax>(a, P, G, st);
     return launch_mode<kStore>(a, P, G, st);
+}
+
+hipError_t launch_repair(const ScanArgs& base, int P, int G, int k, const uint32_t* counts, int64_t cap,
+                         float* rows, int slots, int32_t* topk_idx, float* topk_val, int32_t* sorted_idx,
+                         hipStream_t st)
+{
+    ScanArgs a = base;
+    a.stride = 1;
+    a.nlb = a.nb;
+    a.gb = (int)a.nb;  // one tile: the whole pair
+    a.out = rows;
+    const dim3 grid((unsigned)slots);
+    if (G <= 4) repair_kernel<1><<<grid, kThreads, 0, st>>>(a, P, G, k, counts, cap, topk_idx, topk_val, sorted_idx);
+    else repair_kernel<2><<<grid, kThreads, 0, st>>>(a, P, G, k, counts, cap, topk_idx, topk_val, sorted_idx);
+    return hipGetLastError();
 }
 
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int P, int D, int64_t n,

@@ -188,3 +188,20 @@ def test_binding_refuses_host_tensors():
         F._ptr(torch.zeros(4))
     assert F._ptr(None) is None
     assert F._ptr(4096).value == 4096
+
+
+def test_fused_workspace_is_bounded(L):
+    """The fused scan + top-k keeps a bounded number of full score rows for
+    the heads its sampled threshold misjudges (16 pairs' worth at most), so
+    at 1M tokens x 288 pairs its workspace stays below 1 GiB, a fifth of a
+    full score copy; it grows with the pairs only through the candidate
+    lists."""
+    npad = 1 << 20
+    full = 288 * 4 * npad * 4
+    b288 = L.fathom_scan_topk_workspace_bytes(288, 4, npad, 512)
+    assert 0 < b288 < 1 << 30 and b288 < full // 5
+    b8 = L.fathom_scan_topk_workspace_bytes(8, 4, npad, 512)
+    b16 = L.fathom_scan_topk_workspace_bytes(16, 4, npad, 512)
+    b32 = L.fathom_scan_topk_workspace_bytes(32, 4, npad, 512)
+    assert b8 >= 8 * 4 * npad * 4  # fewer pairs than rows: one row per pair
+    assert b32 - b16 < 16 * 4 * npad * 4  # beyond 16 pairs no more rows

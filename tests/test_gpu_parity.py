@@ -308,6 +308,37 @@ def test_fused_scan_topk_bit_exact(F, orc, kind, n, D, G, budget, k, mode):
         assert_selection_valid(orc, rp, rs, n, ref["depth"], ref["q_used"], idx[p])
 
 
+def test_fused_repair_with_more_failed_pairs_than_rows(F, orc):
+    """Every third pair has an all-zero query, so all its scores tie and its
+    candidate lists overflow; with 37 pairs that is 13 failed pairs, and
+    with 20 of them (every pair) more failures than the 16 repair rows, so
+    each repair workgroup rescans several pairs in turn.  Every pair's
+    top-k and union must equal the oracle's bit for bit."""
+    G, D, n, k, budget = 4, 128, 3000 + 5, 100, 48
+    for P, zero in ((37, lambda p: p % 3 == 0), (20, lambda p: True)):
+        g = np.random.default_rng(P)
+        x = [(g.standard_normal((n, D)) * np.exp(0.5 * g.standard_normal(D))).astype(np.float32)
+             for _ in range(P)]
+        q, s2 = _plan_inputs(P, G, D, 1000 + P)
+        for p in range(P):
+            if zero(p):
+                q[p] = 0.0
+        say("fused repair, failed pairs:", sum(zero(p) for p in range(P)), "of", P)
+        planes, scales = F.pack(dev(np.stack(x)))
+        pl = F.plan(dev(q), dev(s2), budget, 0)
+        out = F.scan_topk(planes, scales, n, pl, k)
+        idx = out.idx.cpu().numpy()
+        val = out.val.cpu().numpy()
+        for p in range(P):
+            rp, rs = orc.pack(x[p])
+            ref = orc.step(rp, rs, n, q[p], s2[p], budget, k)
+            assert np.array_equal(idx[p], ref["topk"]), p
+            for h in range(G):
+                assert np.array_equal(val[p, h], ref["scores"][h][ref["topk"][h]])
+            assert int(out.union_len[p]) == ref["union_len"]
+            assert np.array_equal(out.union[p].cpu().numpy(), ref["union"]), p
+
+
 def _sample_stride(n, k):
     """One run of 32 blocks in every s runs is sampled for the fused
     threshold: s is the largest power of two with (2s)^2 4k <= n kept."""
