@@ -254,6 +254,36 @@ int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t
                            void* stream);
 
 /*
+ * fathom_scan_topk_noalloc -- fathom_scan_topk for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not call the allocator, harnesses that forbid it.  Same arguments and
+ * results as fathom_scan_topk, without ws / ws_bytes: the workspace is a
+ * fixed 128 MiB scratch array inside the library, one per GPU, which this
+ * call neither allocates nor frees (the first call on a device looks up that
+ * device's copy).
+ *
+ * Limit: the call must fit the scratch with at least one repair row, i.e.
+ * fathom_scan_topk_workspace_bytes computed with one row instead of
+ * min(P, 16) must be at most 128 MiB (at G = 4, k = 512: 8 pairs x 4M
+ * tokens, 16 x 2M or 32 x 1M fit, a layer's 8 KV heads at any context up to
+ * 4M; 288 pairs x 1M do not).  Fewer rows than min(P, 16) only slow the rare
+ * repair.  Larger calls return ERR_WORKSPACE before any work is enqueued.
+ *
+ * Every call on a GPU uses that GPU's one scratch array, whose contents are
+ * left over from the last call (nothing in it needs to start at zero): calls
+ * that overlap on one GPU -- on different streams, or from different host
+ * threads -- race and must be serialised by the caller.  The current device
+ * must be the one the pointers and the stream belong to.
+ * Errors: as fathom_scan_topk, with ERR_WORKSPACE for a call too large for
+ * the scratch and ERR_HIP if the scratch cannot be located.
+ */
+int fathom_scan_topk_noalloc(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
+                             int64_t n, int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                             const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                             int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                             void* stream);
+
+/*
  * fathom_gather_rows -- the winner-row fetch that follows the selection:
  * copy the union rows of every pair (the keys and values a decode step
  * attends to, at most G*k rows per KV head) out of a row table that may live

@@ -1,5 +1,7 @@
 // C ABI entry points (declared in include/fathom.h): argument checks on the
 // host, then asynchronous launches on the caller's stream.
+#include <mutex>
+
 #include "../../include/fathom.h"
 #include "common.h"
 
@@ -38,6 +40,32 @@ inline int64_t row_blocks(int64_t n, int64_t nb_cap)
     if (nb_cap == 0) return nb;
     if (nb_cap < nb || nb_cap > kMaxRowBlocks) return -1;
     return nb_cap;
+}
+
+// ---- the fixed scratch of fathom_scan_topk_noalloc.  Each GPU the library
+// runs on holds its own copy of this array until the process ends; host
+// code reaches it only through the device address hipGetSymbolAddress gives
+// for the current device (the array's name on the host is not that address).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // per device ordinal, set on the first call there
+
+int scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FATHOM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FATHOM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FATHOM_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return FATHOM_OK;
 }
 
 }  // namespace
@@ -164,11 +192,13 @@ size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t
     return topk_layout(P, G, n, k).bytes_fused;
 }
 
-static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
-                          int64_t n, int64_t nb_cap, const uint8_t* depth, const int16_t* active,
-                          const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
-                          int32_t* topk_idx, float* topk_val, int32_t* union_idx,
-                          int32_t* union_len, void* ws, size_t ws_bytes, void* stream, int stages)
+// Argument checks shared by the fused entry points; fills the scan's
+// arguments.  Returns FATHOM_OK or the error.
+static int scan_topk_check(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
+                           int64_t n, int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                           const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                           int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                           int stages, ScanArgs& a)
 {
     if (!planes || !scales || !depth || !active || !n_active || !q_used) return FATHOM_ERR_ARG;
     if ((stages & 4) && (!topk_idx || !union_idx || !union_len)) return FATHOM_ERR_ARG;
@@ -189,10 +219,7 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
             if (!aligned16(p)) return FATHOM_ERR_ALIGN;
         if (topk_val && !aligned16(topk_val)) return FATHOM_ERR_ALIGN;
     }
-    const TopkLayout L = topk_layout(P, G, n, k);
-    if (!ws || ws_bytes < L.bytes_fused) return FATHOM_ERR_WORKSPACE;
-    if (!aligned16(ws)) return FATHOM_ERR_ALIGN;
-    ScanArgs a{};
+    a = ScanArgs{};
     a.planes = planes;
     a.scales = scales;
     a.D = D;
@@ -203,6 +230,22 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
     a.active = active;
     a.n_active = n_active;
     a.q_used = q_used;
+    return FATHOM_OK;
+}
+
+static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
+                          int64_t n, int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                          const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                          int32_t* topk_idx, float* topk_val, int32_t* union_idx,
+                          int32_t* union_len, void* ws, size_t ws_bytes, void* stream, int stages)
+{
+    ScanArgs a;
+    const int s = scan_topk_check(planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, k,
+                                  topk_idx, topk_val, union_idx, union_len, stages, a);
+    if (s) return s;
+    const TopkLayout L = topk_layout(P, G, n, k);
+    if (!ws || ws_bytes < L.bytes_fused) return FATHOM_ERR_WORKSPACE;
+    if (!aligned16(ws)) return FATHOM_ERR_ALIGN;
     return hip_status(launch_scan_topk(a, P, G, k, topk_idx, topk_val, union_idx, union_len, ws, L,
                                        stages, (hipStream_t)stream));
 }
@@ -228,6 +271,28 @@ int fathom_scan_topk_stage(int32_t stage, const uint64_t* planes, const uint16_t
     return scan_topk_impl(planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, k,
                           topk_idx, topk_val, union_idx, union_len, ws, ws_bytes, stream,
                           1 << (stage - 1));
+}
+
+int fathom_scan_topk_noalloc(const uint64_t* planes, const uint16_t* scales, int32_t P, int32_t D,
+                             int64_t n, int64_t nb_cap, const uint8_t* depth, const int16_t* active,
+                             const int32_t* n_active, const float* q_used, int32_t G, int32_t k,
+                             int32_t* topk_idx, float* topk_val, int32_t* union_idx, int32_t* union_len,
+                             void* stream)
+{
+    ScanArgs a;
+    int s = scan_topk_check(planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, k,
+                            topk_idx, topk_val, union_idx, union_len, 7, a);
+    if (s) return s;
+    // as many repair rows as the scratch holds, at least one (the results do
+    // not depend on the count: the rows only bound the repair's parallelism)
+    int rows = P < kRepairSlots ? P : kRepairSlots;
+    TopkLayout L = topk_layout(P, G, n, k, rows);
+    while (L.bytes_fused > kScratchBytes && rows > 1) L = topk_layout(P, G, n, k, --rows);
+    if (L.bytes_fused > kScratchBytes) return FATHOM_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((s = scratch_address(&ws)) != FATHOM_OK) return s;
+    return hip_status(launch_scan_topk(a, P, G, k, topk_idx, topk_val, union_idx, union_len, ws, L, 7,
+                                       (hipStream_t)stream));
 }
 
 int fathom_gather_rows(const void* table, int64_t table_rows, int64_t row_bytes,

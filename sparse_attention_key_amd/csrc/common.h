@@ -146,6 +146,10 @@ hipError_t launch_calib_covariance(const void* keys, int dtype, int P, int64_t m
                                    float* var, void* ws, hipStream_t st);
 hipError_t launch_calib_basis(const double* cov, int P, int D, float* U, float* lam, hipStream_t st);
 
+// Repair rows of the fused path: a workgroup per row rescans one failed pair
+// at a time, so this bounds both the workspace and the repair's parallelism.
+constexpr int kRepairSlots = 16;
+
 struct TopkLayout {
     int64_t m;           // selections = P * G
     int64_t stride;      // sample one run of 32 blocks in every `stride` runs
@@ -157,10 +161,8 @@ struct TopkLayout {
     int slots;           // fused: full score rows (pairs) for the repair, reused in turn
     size_t off_sample, off_repair, bytes_fused;  // fused scan + top-k
 };
-// Repair rows of the fused path: a workgroup per row rescans one failed pair
-// at a time, so this bounds both the workspace and the repair's parallelism.
-constexpr int kRepairSlots = 16;
-TopkLayout topk_layout(int P, int G, int64_t n, int k);
+// rows: repair rows of the fused path, at most this many (and at most P)
+TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows = kRepairSlots);
 hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,
                        float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
                        const TopkLayout& L, hipStream_t st);

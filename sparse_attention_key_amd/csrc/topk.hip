@@ -225,7 +225,7 @@ void launch_union(const int32_t* sorted, int P, int G, int k, int32_t* union_idx
 
 }  // namespace
 
-TopkLayout topk_layout(int P, int G, int64_t n, int k)
+TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows)
 {
     TopkLayout L{};
     const int64_t nb = (n + 63) / 64;
@@ -246,7 +246,7 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k)
     L.cap = 8 * (int64_t)k * s + 1024;
     if (L.cap > nb * 64) L.cap = nb * 64;
     L.sample_nlb = ((nb + 32 * s - 1) / (32 * s)) * 32;
-    L.slots = P < kRepairSlots ? P : kRepairSlots;
+    L.slots = P < rows ? P : rows;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     L.off_tau = 0;
     L.off_count = up((size_t)L.m * 4);

@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         L.fathom_scan_topk_workspace_bytes.restype = sz
         L.fathom_scan_topk.argtypes = [P, P, i32, i32, i64, i64, P, P, P, P, i32, i32, P, P, P, P, P, sz, P]
         L.fathom_scan_topk_stage.argtypes = [i32] + L.fathom_scan_topk.argtypes
+        L.fathom_scan_topk_noalloc.argtypes = L.fathom_scan_topk.argtypes[:16] + [P]
         L.fathom_read_probe.argtypes = [P, sz, P, P]
         L.fathom_gather_rows.argtypes = [P, i64, i64, i64, i32, P, P, i32, P, P]
         L.fathom_gather_rows.restype = ctypes.c_int
@@ -66,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.fathom_calib_basis.restype = ctypes.c_int
         L.fathom_read_probe.restype = ctypes.c_int
         for f in (L.fathom_pack, L.fathom_pack_range, L.fathom_plan, L.fathom_scan, L.fathom_topk,
-                  L.fathom_scan_topk, L.fathom_scan_topk_stage):
+                  L.fathom_scan_topk, L.fathom_scan_topk_stage, L.fathom_scan_topk_noalloc):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,15 +204,17 @@ def scan_topk_workspace_bytes(P: int, G: int, n: int, k: int) -> int:
 
 class TopkOut:
     def __init__(self, P: int, G: int, n: int, k: int, device="cuda", with_values=True,
-                 fused: bool = False):
+                 fused: bool = False, workspace: bool = True):
         self.P, self.G, self.n, self.k = P, G, n, k
         self.idx = torch.empty((P, G, k), dtype=torch.int32, device=device)
         self.val = torch.empty((P, G, k), dtype=torch.float32, device=device) if with_values else None
         self.union = torch.empty((P, G * k), dtype=torch.int32, device=device)
         self.union_len = torch.empty((P,), dtype=torch.int32, device=device)
-        ws_fn = scan_topk_workspace_bytes if fused else topk_workspace_bytes
-        nbytes = max(ws_fn(P, G, n, k), 16)
-        self.ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+        self.ws = None  # workspace=False: outputs only (for scan_topk_noalloc_into)
+        if workspace:
+            ws_fn = scan_topk_workspace_bytes if fused else topk_workspace_bytes
+            nbytes = max(ws_fn(P, G, n, k), 16)
+            self.ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
 
 def topk_into(scores, n: int, out: TopkOut, stream=None):
@@ -243,6 +246,17 @@ def scan_topk_into(planes, scales, n: int, pl: Plan, out: TopkOut, stream=None, 
 def scan_topk(planes, scales, n: int, pl: Plan, k: int, stream=None, nb_cap=None) -> TopkOut:
     out = TopkOut(pl.P, pl.G, n, k, pl.q_used.device, fused=True)
     return scan_topk_into(planes, scales, n, pl, out, stream, nb_cap)
+
+
+def scan_topk_noalloc_into(planes, scales, n: int, pl: Plan, out: TopkOut, stream=None, nb_cap=None):
+    """scan_topk_into with the library's fixed per-GPU scratch as workspace
+    (no device allocation; out.ws is not used, so `out` may be a
+    TopkOut(..., workspace=False)).  Calls that overlap on one GPU race."""
+    _check("fathom_scan_topk_noalloc", lib().fathom_scan_topk_noalloc(
+        _ptr(planes), _ptr(scales), pl.P, pl.D, int(n), _nb_cap(planes, nb_cap), _ptr(pl.depth),
+        _ptr(pl.active), _ptr(pl.n_active), _ptr(pl.q_used), pl.G, out.k, _ptr(out.idx), _ptr(out.val),
+        _ptr(out.union), _ptr(out.union_len), _stream(stream)))
+    return out
 
 
 def scan_topk_stage(stage: int, planes, scales, n: int, pl: Plan, out: TopkOut, stream=None,

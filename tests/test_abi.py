@@ -205,3 +205,18 @@ def test_fused_workspace_is_bounded(L):
     b32 = L.fathom_scan_topk_workspace_bytes(32, 4, npad, 512)
     assert b8 >= 8 * 4 * npad * 4  # fewer pairs than rows: one row per pair
     assert b32 - b16 < 16 * 4 * npad * 4  # beyond 16 pairs no more rows
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(L):
+    """fathom_scan_topk_noalloc checks its arguments and the size of the
+    call against its fixed scratch before any HIP call."""
+    args = lambda **kw: [A, A, kw.get("P", 8), 128, kw.get("n", 4096), 0, A, A, A, A, 4, kw.get("k", 64),
+                         A, None, A, A, None]
+    assert L.fathom_scan_topk_noalloc(*args(P=288, n=1 << 20, k=512)) == F.ERR_WORKSPACE
+    assert L.fathom_scan_topk_noalloc(*args(P=8, n=1 << 23, k=512)) == F.ERR_WORKSPACE
+    assert L.fathom_scan_topk_noalloc(*args(k=0)) == F.ERR_ARG
+    assert L.fathom_scan_topk_noalloc(*args(P=0)) == F.ERR_SHAPE
+    a = args()
+    a[0] = None
+    assert L.fathom_scan_topk_noalloc(*a) == F.ERR_ARG
+
