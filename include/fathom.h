@@ -221,7 +221,8 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
  * than their capacity (massive ties) has its pair rescanned into a full
  * score row inside the workspace and is selected from there; results are
  * exact either way.  The rows are min(P, 16) pairs' worth (G * npad floats
- * each): one workgroup per row rescans the failed pairs in turn, so the
+ * each): the first failed pairs are rescanned into them by many workgroups
+ * at once, and any further ones by one workgroup per row in turn, so the
  * workspace does not grow with the number of failures (at 1M tokens x 288
  * pairs, G = 4, k = 512 it is about 0.9 GB).
  *   ws  device workspace of at least fathom_scan_topk_workspace_bytes().

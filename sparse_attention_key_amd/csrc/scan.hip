@@ -744,35 +744,32 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a, int G)
     scan_pair<GR, MODE>(a, (int)blockIdx.y, G, (int)blockIdx.x, (int)blockIdx.y);
 }
 
-// Fused path, stage 3: exact selection of the heads whose candidate list
-// failed (more than cap candidates, or fewer than k).  The failed pairs are
-// numbered in pair order; workgroup w takes those numbered w, w + slots, ...
-// in turn, rescans each whole pair (one tile of every block) into its own
-// row of G x npad scores and selects each failed head over that row, so the
-// workspace holds `slots` rows whatever the number of failures.
-template <int GR>
-__global__ __launch_bounds__(kThreads) void repair_kernel(ScanArgs a, int P, int G, int k,
-                                                          const uint32_t* __restrict__ counts, int64_t cap,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_val,
-                                                          int32_t* __restrict__ sorted_idx)
+// Fused path, stage 3: the heads whose candidate list failed (more than
+// cap candidates, or fewer than k) are selected over a full score row of
+// their pair instead.  Failed pairs are numbered in pair order.
+
+// Whether selection m failed.
+__device__ __forceinline__ bool sel_failed(const uint32_t* counts, int64_t m, int64_t cap, int k)
 {
-    __shared__ SelShared sh;
-    __shared__ int s_fail[kThreads];
+    const int64_t c = counts[m];
+    return c > cap || c < (int64_t)k;
+}
+
+// The pair numbered `nth` among the failed ones, or -1; every thread of the
+// workgroup gets the same answer.
+__device__ int nth_failed_pair(const uint32_t* __restrict__ counts, int P, int G, int64_t cap, int k,
+                               uint32_t nth)
+{
     __shared__ uint32_t s_wsum[kWaves];
+    __shared__ int s_pair;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int64_t npad = a.nlb * 64;
-    float* row = a.out + (size_t)blockIdx.x * G * npad;
-    auto failed = [&](int64_t m) {
-        const int64_t c = counts[m];
-        return c > cap || c < (int64_t)k;
-    };
+    if (threadIdx.x == 0) s_pair = -1;
     uint32_t seen = 0;  // failed pairs before this chunk
     for (int p0 = 0; p0 < P; p0 += kThreads) {
         const int p = p0 + (int)threadIdx.x;
         bool f = false;
         if (p < P)
-            for (int h = 0; h < G; ++h) f |= failed((int64_t)p * G + h);
+            for (int h = 0; h < G; ++h) f |= sel_failed(counts, (int64_t)p * G + h, cap, k);
         const uint64_t b = __ballot(f);
         if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(b);
         __syncthreads();
@@ -781,23 +778,57 @@ __global__ __launch_bounds__(kThreads) void repair_kernel(ScanArgs a, int P, int
             off += w < wave ? s_wsum[w] : 0u;
             nf += s_wsum[w];
         }
-        if (f) s_fail[off + (uint32_t)__popcll(b & lanes_below(lane))] = p;
+        if (f && seen + off + (uint32_t)__popcll(b & lanes_below(lane)) == nth) s_pair = p;
         __syncthreads();
-        for (uint32_t i = 0; i < nf; ++i) {
-            if ((seen + i) % gridDim.x != blockIdx.x) continue;
-            const int fp = s_fail[i];
-            scan_pair<GR, kStore>(a, fp, G, 0, (int)blockIdx.x);
-            __syncthreads();  // the row is complete (and the pair's LDS tables free)
-            for (int h = 0; h < G; ++h) {
-                const int64_t m = (int64_t)fp * G + h;
-                if (!failed(m)) continue;
-                select_one(row + (size_t)h * npad, a.n, npad, true, nullptr, 0, k, m, topk_idx, topk_val,
-                           sorted_idx, sh);
-                __syncthreads();  // sh is reused by the next head
-            }
-        }
+        const int r = s_pair;
+        if (r >= 0 || nth < seen + nf) return r;
         seen += nf;
-        __syncthreads();  // s_fail and s_wsum are rewritten by the next chunk
+        __syncthreads();  // s_wsum is rewritten by the next chunk
+    }
+    return -1;
+}
+
+// (1) Failed pair number r (r < rows) is rescanned into score row r, tile
+// blockIdx.x of it per workgroup, as fast as a scan of that many pairs.
+template <int GR>
+__global__ __launch_bounds__(kThreads) void repair_scan_kernel(ScanArgs a, int P, int G, int k,
+                                                               const uint32_t* __restrict__ counts,
+                                                               int64_t cap)
+{
+    const int fp = nth_failed_pair(counts, P, G, cap, k, blockIdx.y);
+    if (fp < 0) return;
+    scan_pair<GR, kStore>(a, fp, G, (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// (2) Workgroup r selects the failed heads of failed pair r from row r
+// (filled by (1)); then it takes failed pairs r + rows, r + 2 rows, ...,
+// should there be more than rows of them, rescanning each whole pair
+// itself into its row.  The rows bound the workspace whatever the number
+// of failures; only failures beyond the first `rows` pairs are slow.
+template <int GR>
+__global__ __launch_bounds__(kThreads) void repair_select_kernel(ScanArgs a, int P, int G, int k,
+                                                                 const uint32_t* __restrict__ counts,
+                                                                 int64_t cap, int32_t* __restrict__ topk_idx,
+                                                                 float* __restrict__ topk_val,
+                                                                 int32_t* __restrict__ sorted_idx)
+{
+    __shared__ SelShared sh;
+    const int64_t npad = a.nlb * 64;
+    float* row = a.out + (size_t)blockIdx.x * G * npad;
+    for (uint32_t i = blockIdx.x;; i += gridDim.x) {
+        const int fp = nth_failed_pair(counts, P, G, cap, k, i);
+        if (fp < 0) break;
+        if (i >= gridDim.x) {
+            scan_pair<GR, kStore>(a, fp, G, 0, (int)blockIdx.x);  // one tile: a.gb covers the pair
+            __syncthreads();  // the row is complete (and the pair's LDS tables free)
+        }
+        for (int h = 0; h < G; ++h) {
+            const int64_t m = (int64_t)fp * G + h;
+            if (!sel_failed(counts, m, cap, k)) continue;
+            select_one(row + (size_t)h * npad, a.n, npad, true, nullptr, 0, k, m, topk_idx, topk_val,
+                       sorted_idx, sh);
+            __syncthreads();  // sh is reused by the next head
+        }
     }
 }
 
@@ -843,11 +874,19 @@ hipError_t launch_repair(const ScanArgs& base, int P, int G, int k, const uint32
     ScanArgs a = base;
     a.stride = 1;
     a.nlb = a.nb;
-    a.gb = (int)a.nb;  // one tile: the whole pair
     a.out = rows;
-    const dim3 grid((unsigned)slots);
-    if (G <= 4) repair_kernel<1><<<grid, kThreads, 0, st>>>(a, P, G, k, counts, cap, topk_idx, topk_val, sorted_idx);
-    else repair_kernel<2><<<grid, kThreads, 0, st>>>(a, P, G, k, counts, cap, topk_idx, topk_val, sorted_idx);
+    // (1): tiles of the first `slots` failed pairs, sized like a scan of
+    // that many pairs; workgroups of absent failures return at once
+    a.gb = kGroupBlocks;
+    while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * slots < 512) a.gb /= 2;
+    const dim3 g1((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)slots);
+    if (G <= 4) repair_scan_kernel<1><<<g1, kThreads, 0, st>>>(a, P, G, k, counts, cap);
+    else repair_scan_kernel<2><<<g1, kThreads, 0, st>>>(a, P, G, k, counts, cap);
+    // (2): selection, and one workgroup per row for any further failures
+    a.gb = (int)a.nb;
+    const dim3 g2((unsigned)slots);
+    if (G <= 4) repair_select_kernel<1><<<g2, kThreads, 0, st>>>(a, P, G, k, counts, cap, topk_idx, topk_val, sorted_idx);
+    else repair_select_kernel<2><<<g2, kThreads, 0, st>>>(a, P, G, k, counts, cap, topk_idx, topk_val, sorted_idx);
     return hipGetLastError();
 }
 

@@ -27,8 +27,9 @@
 //                overflowed their capacity, or number fewer than k, runs the
 //                same select directly over all its scores instead: over the
 //                given scores, or in the fused path over a full score row
-//                its pair is rescanned into (one workgroup per pair, a
-//                bounded number of rows in the workspace, reused in turn).
+//                its pair is rescanned into (a bounded number of rows in the
+//                workspace: the first failed pairs rescanned by many
+//                workgroups, any further ones by one workgroup per row).
 //  4. union:     merge of the G index-sorted lists of a pair, duplicates
 //                dropped.
 #include "select.h"
