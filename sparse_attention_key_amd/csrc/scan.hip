@@ -57,6 +57,14 @@ constexpr int kRun = 32;                           // sampled blocks come in run
 constexpr int kSlotsMax = 128;
 constexpr int kRec = 32;                           // LDS bytes per (slot, half block) code record
 constexpr int kCodeBytes = 8 * 32 * kRec + 8 * 32;   // 2 (4/C) half blocks of 32 C slots and a spare record
+// Bytes between the wavefronts' record areas.  A record write (16 lanes of
+// 8 bytes per LDS pass: two slots x 8 block pairs, the pairs spread over the
+// four areas) meets distinct banks when the areas are 32 bytes apart modulo
+// the bank span (C = 1 and 2; two-way for C = 4): with no padding the four
+// areas alias and the writes were four-way conflicted (47 conflict cycles
+// per block at 1M tokens x 288 pairs).  Reads stay within one area, so the
+// padding does not change them.
+constexpr int kCodeStride = kCodeBytes + 32;
 constexpr int kCoefBytes = 4 * 32 * 16;            // (4/C) blocks x 32 C slots x 2 head pairs x 8 B
 constexpr int kStage = 128;                        // staged survivors per wavefront (16-byte records)
 
@@ -485,14 +493,16 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int e = (rl >> 1) + 8 * C * k;
-                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
+                // scale 2^-(E+3): exact (a power of two times a binary16 value)
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]) * pw;
 #pragma unroll
                 for (int gr = 0; gr < GR; ++gr) {
                     uint32_t dig[2];
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
-                        // trunc(fl32(q 2^sigma * scale) 2^-(E+3)); q 2^sigma 2^-(E+3) is exact
-                        const int Ai = (int)((qt[k][gr][x] * pw) * sf);
+                        // trunc(fl32(q 2^sigma * scale) 2^-(E+3)): both power-of-two
+                        // factors are exact, so this is that one rounding
+                        const int Ai = (int)(qt[k][gr][x] * sf);
                         dig[x] = ((uint32_t)Ai + 0x00808080u) ^ 0x00808080u;
                     }
                     *(v2i*)(coef + gr * kCoefBytes + rb * (S * 16) + (e * 2 + rhp) * 8) =
@@ -639,13 +649,509 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     if (MODE == kFilter && scnt) flush();
 }
 
+// The same tile with the plane loads shared out by slot (see the comment
+// on the codes below): one 16-byte load per plane and lane covers every
+// block of a workgroup iteration, so each line is requested once, at the
+// price of two workgroup barriers per iteration.  It pays when the slot
+// quarters are about equally deep (fixed-depth plans, and A > 64), and loses
+// to the per-wavefront form when the deep slots sit in one quarter (the
+// others wait for it at the barrier).
+template <int GR, int MODE, int C>
+__device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p, const int G, const int A,
+                                          const int tile, const int op, const PairTables<GR>& T,
+                                          unsigned char* code0, unsigned char* code, unsigned char* coef,
+                                          v4i* stage)
+{
+    constexpr int S = 32 * C, NB = 4 / C;
+    constexpr int NH = 4 * GR;
+    constexpr int IB = kWaves * NB;  // logical blocks the workgroup takes per iteration
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int kap = lane >> 4, j16 = lane & 15;  // lane group (slot block / head) and row
+    // block indices fit 32 bits (the host caps n below 2^31 tokens), and the
+    // plane and scale offsets below fit 31 bits (the host rejects a pair whose
+    // plane rows span 2^31 bytes or more)
+    const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride;
+    // Iteration i of the workgroup reads the plane words of logical blocks
+    // lg0 + i IB .. lg0 + i IB + IB - 1 (each wavefront its own slots), and
+    // wavefront w multiplies and scores blocks lg0 + i IB + w NB + (0 .. NB-1).
+    const int lg0 = tile * a.gb;
+    const int lgend = min(lg0 + a.gb, nlb);
+    const int64_t ldb = a.ldb;
+    const uint32_t ldb8 = (uint32_t)(ldb * 8);
+
+    // the pair's planes and scales; the descriptors are rebased on every
+    // iteration's first physical block, so the range check stays exact
+    const uint64_t* pplanes = a.planes + (size_t)p * a.D * 4 * ldb;
+    const uint16_t* pscales = a.scales + (size_t)p * a.D * ldb;
+    const uint32_t pbytes = (uint32_t)((int64_t)a.D * 4 * ldb * 8);
+    const uint32_t sbytes = (uint32_t)((int64_t)a.D * ldb * 2);
+    constexpr uint32_t kOOB = 0x80000000u;  // past every record: the load returns 0
+    // (the record count is formed with a signed max: a saturating subtract
+    // would be computed per lane and turn the descriptor into a per-lane value)
+    auto records = [](uint32_t total, uint32_t off, bool live) {
+        return __builtin_amdgcn_readfirstlane(live ? max((int)total - (int)off, 0) : 0);
+    };
+    // plane s of a row is read at the row's plane-0 offset (per lane) plus
+    // s * ldb * 8 (the scalar offset); a lane whose block lies past the
+    // index is pointed out of range (see `mask_dead`), so no read ever leaves
+    // the pair's planes, whether or not the range check counts the scalar offset
+    auto plane_rsrc = [&](int pb0, bool live) {
+        const uint32_t off = (uint32_t)pb0 * 8u;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)pplanes + off), (short)0,
+                                                 records(pbytes, off, live), 0x00020000);
+    };
+    auto scale_rsrc = [&](int pb0, bool live) {
+        const uint32_t off = (uint32_t)pb0 * 2u;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)pscales + off), (short)0,
+                                                 records(sbytes, off, live), 0x00020000);
+    };
+
+    // ---- codes.  The workgroup's IB blocks of an iteration are shared out
+    // by slot: wavefront w extracts slots 8C w .. 8C w + 8C - 1 (its steps
+    // C w .. C w + C - 1, deepest first) of all IB blocks, lane L taking
+    // slot 8C w + L / (8/C) and the block pair 2 (L % (8/C)) + {0, 1}.  One
+    // 16-byte load per plane then covers the row segments of all IB blocks
+    // (a whole 128-byte line for C = 1), so each line is requested once;
+    // the records are written where the wavefront that multiplies the block
+    // reads them, behind a workgroup barrier.
+    constexpr int LPR = 8 / C;  // lanes per row segment (block pairs per iteration)
+    const int wsl = lane / LPR, wbp = lane % LPR;
+    // which quarter of the slots this wavefront extracts: rotated from one
+    // workgroup to the next, so that the deep slots (more planes) do not
+    // always fall to the same wavefront position, i.e. the same SIMD
+    const int wq = (wave + tile + p) & 3;
+    const int we = 8 * C * wq + wsl;  // the lane's slot
+    const int wt = (int)(T.slot[we] >> 8);
+    const int wj = (int)(T.slot[we] & 255u);
+    // the deepest slot of the quarter (slots are sorted deepest first)
+    const int wtm = __builtin_amdgcn_readfirstlane((int)(T.slot[8 * C * wq] >> 8));
+    // the lane's plane-3 row ends the pair's planes: a 16-byte read of its
+    // last block pair would pass that end (see `mask_dead`)
+    const bool wlast = wt == 4 && wj == a.D - 1;
+    // record write offsets: record (block pair half i, half block hs) of the
+    // lane, chunk rho, is at wr[rho] + i * kPairStep + hs * H in s_code
+    constexpr uint32_t kPairStep = C == 4 ? (uint32_t)kCodeStride : 2u * (uint32_t)kHalfBytes<C>;
+    uint32_t wr[4];
+    {
+        const int b0 = 2 * wbp, cw = b0 / NB, bl = b0 % NB;
+        const int sk = rec_skew(we, bl);
+        const uint32_t base = (uint32_t)(cw * kCodeStride + 2 * bl * kHalfBytes<C> + we * kRec);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) wr[m] = base + (uint32_t)(((m + sk) & 3) * 8);
+    }
+    // transposing read offsets: read r of tile (b, rho) is rd[r][(rho + 2 (b/2)) & 3] + 2 b H
+    uint32_t rd[C][4];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        const int e = 32 * r + 8 * kap + (j16 >> 1), hs = j16 & 1;
+        const int sk = rec_skew(e, 0);
+        const uint32_t base = (uint32_t)(hs * kHalfBytes<C> + e * kRec);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) rd[r][m] = base + (uint32_t)(((m + sk) & 3) * 8);
+    }
+    // ---- digit rows: the 16C lanes of block L / 16C compute its (slot,
+    // head pair) rows pi = L % 16C + 16C k, k = 0..3 (slot pi / 2, pair L & 1)
+    constexpr int LPB = 16 * C;
+    const int rb = lane / LPB, rl = lane % LPB, rhp = lane & 1;
+    uint32_t srow[4];  // scale byte offset of slot k from the iteration's first block (out of range past A)
+    float qt[4][GR][2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = (rl >> 1) + 8 * C * k;
+        const int j = (int)(T.slot[e] & 255u);
+        srow[k] = e < A ? (uint32_t)j * (uint32_t)(ldb * 2) + (uint32_t)rb * 2u : kOOB;
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int h = 4 * gr + 2 * rhp + x;
+                qt[k][gr][x] = (e < A && h < G)
+                    ? __builtin_ldexpf(T.qv[h][j], T.sig[h]) : 0.0f;
+            }
+    }
+    // constants column of read r: slots 32 r + 8 kap + 0..7
+    v2i dcol[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dcol[r] = r < C ? *(const v2i*)(T.d + 32 * r + 8 * kap) : (v2i){0, 0};
+    // screen margins (hi units, 2^16): the two lower digit sums of a tile of
+    // weight 2^rho are bounded by 15 2^rho (128 * 256 + 128) A, those of the
+    // block constant by 15 (128 * 256 + 128) A
+    const float lob = 7.53f * (float)A + 1.0f;
+    // per-lane heads kap + 4 gr
+    float thr[GR], pth[GR];
+    int sig[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+        const int h = kap + 4 * gr;
+        sig[gr] = T.sig[h];
+        thr[gr] = pth[gr] = INFINITY;
+        if (MODE == kFilter && h < G) {
+            const uint32_t tk = a.tau[(size_t)p * G + h];
+            const float th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
+            thr[gr] = th;
+            // next float below the threshold: a score >= th has S 2^zeta above it
+            pth[gr] = th == -INFINITY ? -INFINITY
+                    : th > 0.0f  ? __uint_as_float(__float_as_uint(th) - 1u)
+                    : th == 0.0f ? -1.40129846e-45f
+                                 : __uint_as_float(__float_as_uint(th) + 1u);
+        }
+    }
+    // FILTER: screened tokens wait in this wavefront's stage as (exact sum,
+    // token, head | exponent << 16) records; a flush turns them into scores,
+    // keeps those at or above their head's threshold, and appends them to the
+    // candidate lists with one fetch-and-add per head
+    uint32_t scnt = 0;  // wavefront-uniform
+    auto flush = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (uint32_t r0 = 0; r0 < scnt; r0 += kWave) {
+            const bool valid = r0 + (uint32_t)lane < scnt;
+            v4i rec = valid ? stage[r0 + lane] : (v4i){0, 0, 0, 0};
+            const int h = rec.w & 0xFF, zeta = rec.w >> 16;
+            const int64_t S = (int64_t)(((uint64_t)(uint32_t)rec.y << 32) | (uint32_t)rec.x);
+            const float sc = (float)__builtin_ldexp((double)S, zeta);
+            const bool keep = valid && sc >= T.thr[h];
+            const uint64_t cv = composite(score_key(sc), (uint32_t)rec.z);
+            uint32_t nh = 0, mine = 0;
+            uint64_t mh[NH];
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+                mh[hh] = __builtin_amdgcn_ballot_w64(keep && h == hh);
+                if (lane == hh) nh = (uint32_t)__popcll(mh[hh]);
+                if (h == hh) mine = (uint32_t)__popcll(mh[hh] & lanes_below(lane));
+            }
+            uint32_t base = 0;
+            if (lane < NH && lane < G && nh) base = atomicAdd(&a.counts[(size_t)p * G + lane], nh);
+            const uint32_t bh = (uint32_t)__shfl((int)base, h, kWave);
+            if (keep && (int64_t)(bh + mine) < a.cap) a.cand[((size_t)p * G + h) * a.cap + bh + mine] = cv;
+        }
+        scnt = 0;
+    };
+    // lanes of existing heads, per head group
+    uint64_t hmask[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) hmask[gr] = __builtin_amdgcn_ballot_w64(kap + 4 * gr < G);
+    // token offset (within its block) of this lane's column in chunk rho
+    int toff[4];
+#pragma unroll
+    for (int rho = 0; rho < 4; ++rho) {
+        const int x = j16 & 7;
+        const int g = x < 4 ? (rho == 0 ? 3 : rho - 1) : (rho == 0 ? 7 : rho + 3);
+        toff[rho] = 32 * (j16 >> 3) + g + 8 * (x & 3);
+    }
+    // digit-tile read offset (block 0) of read r
+    uint32_t arow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) arow[r] = (uint32_t)(((32 * r + 8 * kap + (j16 >> 1)) * 2 + (j16 & 1)) * 8);
+
+    // physical block of a logical one: runs of kRun, one run in every stride.
+    // The NB blocks of an iteration lie in one run, so they are consecutive;
+    // blocks past the index read as zeros (the buffer bound) and are masked.
+    auto phys = [&](int lb) { return __builtin_amdgcn_readfirstlane((lb / kRun) * kRun * stride + (lb % kRun)); };
+    // per-lane offset of plane s of the lane's row segment; a plane the slot
+    // does not read gets bit 31 set, which is out of range (kept in vector
+    // registers: a per-plane lane mask would take scalar registers for the
+    // whole loop)
+    uint32_t vo[4];
+    {
+        const uint32_t row = wt ? (uint32_t)wj * 4u * ldb8 + (uint32_t)wbp * 16u : 0u;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            vo[s] = (row + (uint32_t)s * ldb8) | (~(uint32_t)(s - wt) & kOOB);
+            asm volatile("" : "+v"(vo[s]));
+        }
+    }
+    // Last iterations of a pair (the workgroup's base pw0 + IB past the
+    // index): block pairs that lie wholly past the index read nothing; and a
+    // 16-byte read of the pair's very last plane row at its last block would
+    // cross the end of the pair's planes, where the range check drops the
+    // whole read -- it is moved back 8 bytes (the block then sits in the
+    // upper half, see `fix_shift`).  Blocks past the index in the other rows
+    // read neighbouring memory of the pair and are masked by their token
+    // counts.  Returns whether a lane was moved.
+    bool shifted = false;
+    auto mask_dead = [&](int pw0) {
+        if (pw0 + IB > nbk) {
+            const int fb = pw0 + 2 * wbp;  // the lane's first block
+            const uint32_t dead = fb < nbk ? 0u : kOOB;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) vo[s] |= dead;
+            if (wlast && fb < nbk && fb + 1 >= (int)ldb) {
+                vo[3] -= 8u;
+                shifted = true;
+            }
+        }
+    };
+    auto fix_shift = [&](v4i (&w)[4]) {
+        if (shifted) {
+            w[3].x = w[3].z;
+            w[3].y = w[3].w;
+        }
+    };
+    // codes of the lane's four half blocks to LDS; plane s of record
+    // (i, hs) is component 2 i + hs of w[s]
+    auto codes_to_lds = [&](const v4i (&w)[4], unsigned char* code0) {
+        if (wtm == 0) return;  // no slot of this wavefront is read: its stale records meet zero coefficients
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                const int c = 2 * i + hs;
+                const uint32_t hw[4] = {(uint32_t)w[0][c], (uint32_t)w[1][c], (uint32_t)w[2][c],
+                                        (uint32_t)w[3][c]};
+                v2i ch[4];
+                extract(hw, wtm, ch);
+#pragma unroll
+                for (int rho = 0; rho < 4; ++rho)
+                    *(v2i*)(code0 + wr[rho] + i * kPairStep + hs * kHalfBytes<C>) = ch[rho];
+            }
+    };
+
+    // the products of block b of the current iteration (digits and codes in LDS)
+    auto products = [&](int b, v4i (&kk)[GR], v4i (&o)[4][GR]) {
+        v2i ac[GR][4];
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ac[gr][r] = r < C ? tr8(coef + gr * kCoefBytes, (uint32_t)(b * (S * 16)) + arow[r]) : (v2i){0, 0};
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) kk[gr] = mfma_k(ac[gr], dcol, C);
+        v2i bc[4][4];
+#pragma unroll
+        for (int rho = 0; rho < 4; ++rho)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                bc[rho][r] = r < C ? tr8(code, rd[r][(rho + 2 * (b >> 1)) & 3] + (uint32_t)(2 * b * kHalfBytes<C>))
+                                   : (v2i){0, 0};
+#pragma unroll
+        for (int rho = 0; rho < 4; ++rho)
+#pragma unroll
+            for (int gr = 0; gr < GR; ++gr) o[rho][gr] = mfma_k(ac[gr], bc[rho], C);
+    };
+    // Screen, per tile rho: a token whose exact S passes has fl(hi) >= hv =
+    // 2^(rho-1) (P - K) / 2^16 - bound(lo), with P = pred(th) 2^-zeta; hv is
+    // a float lower bound of that.
+    auto screen = [&](const v4i (&kk)[GR], int Eb, float (&hv)[GR][4]) {
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+            const float phi = __builtin_ldexpf(pth[gr], sig[gr] - 15 - Eb);
+            const float z = phi - (float)(kk[gr].z + kk[gr].w * 256);
+            const float zf = z - lob - 4.0f - fabsf(z) * (1.0f / 262144.0f);
+#pragma unroll
+            for (int rho = 0; rho < 4; ++rho)
+                hv[gr][rho] = __builtin_fmaf(zf, rho == 0 ? 0.5f : (float)(1 << (rho - 1)),
+                                             -(lob * (float)(1 << rho) + 2.0f));
+        }
+    };
+
+    // Loads run one iteration ahead, into the registers just consumed: the
+    // scales are used (and the next ones requested) first, then the plane
+    // words once their codes are in LDS.  Every iteration issues the same
+    // 4 + 4 loads -- a plane that the lane's slot does not read is requested
+    // out of range, which costs no memory access -- so the compiler's waits
+    // are exact.
+    auto issue_scales = [&](int pb0, bool live, uint32_t (&sn)[4]) {
+        const __amdgpu_buffer_rsrc_t rs = scale_rsrc(pb0, live);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sn[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, srow[k], 0, 0);
+    };
+    v4i w[4];
+    uint32_t sc[4];
+    {
+        const int pw0 = phys(lg0);
+        mask_dead(pw0);
+        const __amdgpu_buffer_rsrc_t r = plane_rsrc(pw0, true);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, vo[s], 0, 0));
+        issue_scales(phys(lg0 + wave * NB), true, sc);
+    }
+    for (int lw0 = lg0; lw0 < lgend; lw0 += IB) {
+        const int lb0 = lw0 + wave * NB;  // this wavefront's blocks (products, scales, outputs)
+        const bool more = lw0 + IB < lgend;
+        const bool tail = phys(lw0) + IB > nbk;  // blocks past the index (see `mask_dead`)
+        const int pb0 = phys(lb0), pbn = more ? phys(lb0 + IB) : 0;  // past the end: zero records, nothing is read
+        const int pwn = more ? phys(lw0 + IB) : 0;
+        int nval[NB];  // valid tokens of block b (0 for dead blocks)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int64_t left = a.n - (int64_t)(pb0 + b) * 64;
+            nval[b] = (lb0 + b < nlb && pb0 + b < nbk) ? (int)(left < 64 ? left : 64) : 0;
+        }
+
+        // ---- block exponents: largest exponent field of the read scales (>= 1);
+        // fp16 bit patterns of non-negative values order like the values
+        uint32_t mx = max(max(sc[0], sc[1]), max(sc[2], sc[3])) & 0xFFFFu;
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x141, 0xF, 0xF, false));  // row_half_mirror
+        mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xF, 0xF, false));  // row_mirror
+        if (C >= 2) mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, kWave));
+        if (C >= 4) mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, kWave));
+        const int ef = max(1, (int)(mx >> 10) & 31);
+        int Eb[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Eb[b] = __builtin_amdgcn_readlane(ef, b * LPB) - 15;
+        const int Erow = ef - 15;  // the lane's own block
+
+        // ---- digit rows to LDS
+        {
+            const float pw = __uint_as_float((uint32_t)(127 - Erow - 3) << 23);  // 2^-(E+3)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = (rl >> 1) + 8 * C * k;
+                // scale 2^-(E+3): exact (a power of two times a binary16 value)
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]) * pw;
+#pragma unroll
+                for (int gr = 0; gr < GR; ++gr) {
+                    uint32_t dig[2];
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        // trunc(fl32(q 2^sigma * scale) 2^-(E+3)): both power-of-two
+                        // factors are exact, so this is that one rounding
+                        const int Ai = (int)(qt[k][gr][x] * sf);
+                        dig[x] = ((uint32_t)Ai + 0x00808080u) ^ 0x00808080u;
+                    }
+                    *(v2i*)(coef + gr * kCoefBytes + rb * (S * 16) + (e * 2 + rhp) * 8) =
+                        (v2i){(int)dig[0], (int)dig[1]};
+                }
+            }
+        }
+        issue_scales(pbn, more, sc);
+        // ---- codes to LDS, then the next iteration's plane words
+        if (tail) fix_shift(w);
+        if (wq == 0) __builtin_amdgcn_s_setprio(3);  // the deepest slots: the others wait on it
+        codes_to_lds(w, code0);
+        shifted = false;
+        if (more) mask_dead(pwn);
+        {
+            const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pwn, more);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rn, vo[s], 0, 0));
+        }
+        __syncthreads();  // every wavefront's records (and digit rows) are in LDS
+        __builtin_amdgcn_s_setprio(0);
+
+        // ---- products per block; block b+1's products are started before
+        // block b is screened, so they run under its screen and staging
+        v4i kkn[GR], on[4][GR];
+        products(0, kkn, on);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int lb = lb0 + b;
+            v4i kk[GR], o[4][GR];
+#pragma unroll
+            for (int gr = 0; gr < GR; ++gr) {
+                kk[gr] = kkn[gr];
+#pragma unroll
+                for (int rho = 0; rho < 4; ++rho) o[rho][gr] = on[rho][gr];
+            }
+            if (b + 1 < NB) products(b + 1, kkn, on);
+            if (MODE == kFilter) {
+                float hv[GR][4];
+                screen(kk, Eb[b], hv);
+                // lanes whose (head, token) passes the screen, as wavefront masks
+                uint64_t m[4][GR], mor = 0;
+#pragma unroll
+                for (int rho = 0; rho < 4; ++rho)
+#pragma unroll
+                    for (int gr = 0; gr < GR; ++gr) {
+                        m[rho][gr] = __builtin_amdgcn_ballot_w64((float)(o[rho][gr].z + o[rho][gr].w * 256) >=
+                                                                 hv[gr][rho]) & hmask[gr];
+                        mor |= m[rho][gr];
+                    }
+                if (mor) {  // rare: the exact sums of the screened tokens go to the stage
+                    if (nval[b] != 64) {  // the last block of a pair: drop its padding tokens
+                        mor = 0;
+#pragma unroll
+                        for (int rho = 0; rho < 4; ++rho) {
+                            const uint64_t vm = __builtin_amdgcn_ballot_w64(toff[rho] < nval[b]);
+#pragma unroll
+                            for (int gr = 0; gr < GR; ++gr) {
+                                m[rho][gr] &= vm;
+                                mor |= m[rho][gr];
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int gr = 0; gr < GR; ++gr) {
+                        const int64_t Kc = recombine(kk[gr]);
+                        const uint32_t tag = (uint32_t)(kap + 4 * gr) | ((uint32_t)(Eb[b] - 1 - sig[gr]) << 16);
+#pragma unroll
+                        for (int rho = 0; rho < 4; ++rho) {
+                            const uint64_t mm = m[rho][gr];
+                            if (!mm) continue;
+                            const uint32_t np = (uint32_t)__popcll(mm);
+                            if (scnt + np > (uint32_t)kStage) flush();
+                            if ((mm >> lane) & 1u) {
+                                const int64_t x = recombine(o[rho][gr]);
+                                const int64_t S = (rho == 0 ? x * 2 : (x >> (rho - 1))) + Kc;
+                                const uint32_t tok = (uint32_t)(pb0 + b) * 64u + (uint32_t)toff[rho];
+                                stage[scnt + (uint32_t)__popcll(mm & lanes_below(lane))] =
+                                    (v4i){(int)(uint32_t)S, (int)(uint32_t)((uint64_t)S >> 32), (int)tok, (int)tag};
+                            }
+                            scnt += np;
+                        }
+                    }
+                }
+            } else {
+                if (MODE == kStore) {
+#pragma unroll
+                    for (int rho = 0; rho < 4; ++rho) {
+                        const bool tval = toff[rho] < nval[b];
+#pragma unroll
+                        for (int gr = 0; gr < GR; ++gr) {
+                            const int h = kap + 4 * gr;
+                            const float sc = exact_score(o[rho][gr], recombine(kk[gr]), rho, Eb[b] - 1 - sig[gr]);
+                            if (h < G && lb < nlb)
+                                a.out[((size_t)op * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
+                                    tval ? sc : -INFINITY;
+                        }
+                    }
+                } else {
+                    // Maxima of 16 tokens from the top two digit rows (S ~ 2^(17-rho)
+                    // hi + K): the sample is only a statistic for the threshold, whose
+                    // exactness the candidate count check keeps, so an estimate
+                    // within a few units in 2^16 of the exact sum serves.
+#pragma unroll
+                    for (int gr = 0; gr < GR; ++gr) {
+                        const float Kf = __builtin_fmaf((float)(kk[gr].z + kk[gr].w * 256), 65536.0f,
+                                                        (float)(kk[gr].x + kk[gr].y * 256));
+                        float v = -INFINITY;
+#pragma unroll
+                        for (int rho = 0; rho < 4; ++rho) {
+                            const float e = __builtin_fmaf((float)(o[rho][gr].z + o[rho][gr].w * 256),
+                                                           (float)(1 << (17 - rho)), Kf);
+                            v = nval[b] == 64 || toff[rho] < nval[b] ? fmaxf(v, e) : v;
+                        }
+                        v = __builtin_ldexpf(v, Eb[b] - 1 - sig[gr]);
+                        // lanes 4q .. 4q+3 of a head hold one group of 16 tokens
+                        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+                        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+                        const int h = kap + 4 * gr;
+                        if ((j16 & 3) == 0 && h < G && lb < nlb)
+                            a.out[((size_t)op * G + h) * (a.nlb * 4) + (int64_t)lb * 4 + (j16 >> 2)] = v;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the records are read: the next iteration rewrites them
+    }
+    if (MODE == kFilter && scnt) flush();
+}
+
 template <int GR, int MODE>
 __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const int G, const int tile,
                                           const int op)
 {
     constexpr int NH = 4 * GR;
     __shared__ PairTables<GR> T;
-    __shared__ __attribute__((aligned(16))) unsigned char s_code[kWaves][kCodeBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_code[kWaves][kCodeStride];
     __shared__ __attribute__((aligned(16))) unsigned char s_coef[kWaves][GR * kCoefBytes];
     __shared__ v4i s_stage[MODE == kFilter ? kWaves : 1][MODE == kFilter ? kStage : 1];
 
@@ -732,9 +1238,18 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
     unsigned char* code = s_code[wave];
     unsigned char* coef = s_coef[wave];
     v4i* stage = s_stage[MODE == kFilter ? wave : 0];
-    if (A <= 32) scan_body<GR, MODE, 1>(a, p, G, A, tile, op, T, code, coef, stage);
-    else if (A <= 64) scan_body<GR, MODE, 2>(a, p, G, A, tile, op, T, code, coef, stage);
-    else scan_body<GR, MODE, 4>(a, p, G, A, tile, op, T, code, coef, stage);
+    // the four slot quarters equally deep (the deepest slot of the last
+    // quarter as deep as the first), or A > 64: loads shared out by slot
+    const int C = A <= 32 ? 1 : A <= 64 ? 2 : 4;
+    const bool shared = C == 4 || (T.slot[0] >> 8) == (T.slot[24 * C] >> 8);
+    if (shared) {
+        if (C == 1) scan_body_shared<GR, MODE, 1>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
+        else if (C == 2) scan_body_shared<GR, MODE, 2>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
+        else scan_body_shared<GR, MODE, 4>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
+    } else {
+        if (C == 1) scan_body<GR, MODE, 1>(a, p, G, A, tile, op, T, code, coef, stage);
+        else scan_body<GR, MODE, 2>(a, p, G, A, tile, op, T, code, coef, stage);
+    }
 }
 
 // blockIdx.y is the pair, blockIdx.x its tile of gb logical blocks.
