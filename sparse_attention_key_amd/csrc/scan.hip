@@ -1357,14 +1357,16 @@ hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
     // `target`.  Long ranges spread each workgroup's start-up (the pair's
     // tables, the first loads, the last flush) over more blocks: at 1M
     // tokens x 288 pairs the filtered scan takes 1.10 ms with 256 blocks per
-    // workgroup, 0.98 with 512, 0.96 with 1024 and 1.00 with 2048.  For the full
-    // scans (filter, scores) a grid of about two workgroups per CU is best
-    // when the pairs are few: at 1M tokens x 8 pairs (one layer) the filter
-    // takes 110 us with 2048 workgroups of 64 blocks, 77 with 1024, 56 with
-    // 512 and 64 with 256.  The sampled stage reads one
-    // run in 16, so its workgroups are short and more of them (2048) keep the
-    // chip busy: 0.105 ms at 288 pairs against 0.125 with 512.
-    const int64_t target = MODE == kLaneMax ? 2048 : 512;
+    // workgroup, 0.98 with 512, 0.96 with 1024 and 1.00 with 2048.  For the
+    // full scans (filter, scores) of few pairs a grid of about two
+    // workgroups per CU is best: at 1M tokens x 8 pairs (one layer) the
+    // filter takes 110 us with 2048 workgroups of 64 blocks, 77 with 1024,
+    // 56 with 512 and 64 with 256.  Many pairs of shorter rows want the
+    // larger grid: at 131k tokens x 288 pairs 2304 workgroups of 256 blocks
+    // filter in 0.19 ms against 0.22 for 576 of 1024.  The sampled stage
+    // reads one run in 16, so its workgroups are short and more of them
+    // (2048) keep the chip busy: 0.105 ms at 288 pairs against 0.125 with 512.
+    const int64_t target = MODE == kLaneMax || rows >= 64 ? 2048 : 512;
     a.gb = kGroupBlocks;
     while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < target) a.gb /= 2;
     dim3 grid((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)rows);
