@@ -168,6 +168,32 @@ def test_scan_bit_exact_and_within_tolerance(F, orc, n, D, G, mode, budget):
         assert np.all(np.abs(scores[p][:, :n] - d64) <= score_tol(d64, rq, rs))
 
 
+@pytest.mark.parametrize("mode,budget", [(1, 32), (1, 56), (2, 4)])
+def test_scan_reads_the_last_plane_row_at_an_odd_block_count(F, orc, mode, budget):
+    """Plans whose slot groups are equally deep take the scan form that reads
+    two blocks per 16-byte load; the pair's very last plane row (channel
+    D-1, plane 3) ends at an odd block count, so that load is moved back 8
+    bytes.  Channel D-1 is made the most energetic so the fixed plans read
+    it at depth 4 (A = 32, 56 and 128: all three slot-group widths)."""
+    P, G, D, n = 2, 4, 128, 64 * 8 + 9  # 9 blocks
+    g = np.random.default_rng(mode * 100 + budget)
+    x = [(g.standard_normal((n, D)) * np.exp(0.5 * g.standard_normal(D))).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, 321 + budget)
+    q[:, :, D - 1] = 40.0
+    say("scan, last plane row at an odd block count", mode, budget)
+    planes, scales = F.pack(dev(np.stack(x)))
+    pl = F.plan(dev(q), dev(s2), budget, mode)
+    assert int(pl.depth[0, D - 1]) == 4 and int(pl.depth[1, D - 1]) == 4
+    scores = F.scan(planes, scales, n, pl).cpu().numpy()
+    out = F.scan_topk(planes, scales, n, pl, 64)
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        ref = orc.step(rp, rs, n, q[p], s2[p], budget, 64, mode=mode)
+        assert np.array_equal(scores[p].view(np.uint32), ref["scores"].view(np.uint32))
+        assert np.array_equal(out.idx[p].cpu().numpy(), ref["topk"])
+        assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+
+
 def _topk_check(F, orc, s, n, k):
     P, G, _ = s.shape
     out = F.topk(dev(s), n, k)
