@@ -1278,6 +1278,7 @@ __device__ int nth_failed_pair(const uint32_t* __restrict__ counts, int P, int G
     __shared__ uint32_t s_wsum[kWaves];
     __shared__ int s_pair;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
+    __syncthreads();  // a previous call's readers of s_pair and s_wsum are done
     if (threadIdx.x == 0) s_pair = -1;
     uint32_t seen = 0;  // failed pairs before this chunk
     for (int p0 = 0; p0 < P; p0 += kThreads) {
