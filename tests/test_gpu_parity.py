@@ -334,6 +334,44 @@ def test_fused_scan_topk_bit_exact(F, orc, kind, n, D, G, budget, k, mode):
         assert_selection_valid(orc, rp, rs, n, ref["depth"], ref["q_used"], idx[p])
 
 
+def _random_fused_cases(count=24, seed=20261203):
+    """Seeded random shapes for the fused path: n from 1 to 20,000 (ragged
+    blocks), D from 16 to 128 (not only multiples of 8 or 32), G from 1 to 8,
+    every plan mode with a budget across its whole range, k from 1 to
+    min(n, 2048, 16384 / G)."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        n = int(g.integers(1, 20001)) if i % 3 else int(g.integers(1, 400))
+        D = int(g.choice([16, 33, 48, 64, 100, 127, 128]))
+        G = int(g.integers(1, 9))
+        mode = int(g.choice([0, 0, 0, 1, 2]))
+        budget = int(g.integers(0, 4 * D + 1)) if mode == 0 else int(g.integers(0, D + 1)) if mode == 1 \
+            else int(g.integers(0, 5))
+        k = int(g.integers(1, min(n, 2048, 16384 // G) + 1))
+        cases.append((n, D, G, budget, k, mode))
+    return cases
+
+
+@pytest.mark.parametrize("n,D,G,budget,k,mode", _random_fused_cases())
+def test_fused_random_shapes_bit_exact(F, orc, n, D, G, budget, k, mode):
+    P = 2
+    g = np.random.default_rng(n * 131 + D * 7 + G + budget * 3 + k)
+    x = [(g.standard_normal((n, D)) * np.exp(0.7 * g.standard_normal(D))).astype(np.float32) for _ in range(P)]
+    q, s2 = _plan_inputs(P, G, D, n + 3)
+    say("fused random shape", n, D, G, budget, k, mode)
+    planes, scales = F.pack(dev(np.stack(x)))
+    pl = F.plan(dev(q), dev(s2), budget, mode)
+    out = F.scan_topk(planes, scales, n, pl, k)
+    idx = out.idx.cpu().numpy()
+    for p in range(P):
+        rp, rs = orc.pack(x[p])
+        ref = orc.step(rp, rs, n, q[p], s2[p], budget, k, mode=mode)
+        assert np.array_equal(idx[p], ref["topk"]), p
+        assert int(out.union_len[p]) == ref["union_len"]
+        assert np.array_equal(out.union[p].cpu().numpy(), ref["union"])
+
+
 def test_fused_repair_with_more_failed_pairs_than_rows(F, orc):
     """Every third pair has an all-zero query, so all its scores tie and its
     candidate lists overflow; with 37 pairs that is 13 failed pairs, and
