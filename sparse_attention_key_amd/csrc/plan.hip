@@ -59,8 +59,41 @@ __global__ __launch_bounds__(64) void plan_kernel(const float* __restrict__ q,
     __shared__ float s_q[kMaxG][kMaxD];
     __shared__ float s_sq[kMaxD];
     const int p = blockIdx.x, lane = lane_id();
-    for (int e = lane; e < G * D; e += kWave) s_q[e / D][e % D] = q[(size_t)p * G * D + e];
-    __syncthreads();
+    // every query value and variance the lane needs is requested at once (a
+    // lane past D reads channel D - 1, a head past G head G - 1, and drops
+    // them), so the kernel waits for one round trip to memory
+    int jc[2];
+    float qv[2][kMaxG], sg[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int j = lane + c * kWave;
+        jc[c] = j < D ? j : D - 1;
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+            qv[c][h] = q[((size_t)p * G + (h < G ? h : G - 1)) * D + jc[c]];
+        sg[c] = sigma2[(size_t)p * D + jc[c]];
+    }
+    if (rot) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            if (lane + c * kWave < D)
+#pragma unroll
+                for (int h = 0; h < kMaxG; ++h)
+                    if (h < G) s_q[h][lane + c * kWave] = qv[c][h];
+        __syncthreads();
+        const float* U = rot + (size_t)p * D * D;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if (lane + c * kWave >= D) continue;
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) {
+                if (h >= G) break;
+                float acc = 0.0f;
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(U[(size_t)d * D + jc[c]], s_q[h][d], acc);
+                qv[c][h] = acc;
+            }
+        }
+    }
 
     float w[2] = {0.0f, 0.0f}, sq[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -68,21 +101,14 @@ __global__ __launch_bounds__(64) void plan_kernel(const float* __restrict__ q,
         const int j = lane + c * kWave;
         if (j >= D) continue;
         float acc_sq = 0.0f;
-        for (int h = 0; h < G; ++h) {
-            float qu;
-            if (rot) {
-                const float* U = rot + (size_t)p * D * D;
-                float acc = 0.0f;
-                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(U[(size_t)d * D + j], s_q[h][d], acc);
-                qu = acc;
-            } else {
-                qu = s_q[h][j];
-            }
-            q_used[((size_t)p * G + h) * D + j] = qu;
-            acc_sq = __builtin_fmaf(qu, qu, acc_sq);
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h >= G) break;
+            q_used[((size_t)p * G + h) * D + j] = qv[c][h];
+            acc_sq = __builtin_fmaf(qv[c][h], qv[c][h], acc_sq);
         }
         sq[c] = acc_sq;
-        const float v = sigma2[(size_t)p * D + j] * acc_sq;
+        const float v = sg[c] * acc_sq;
         w[c] = (v > 0.0f) ? v : 0.0f;
         s_sq[j] = acc_sq;
     }
