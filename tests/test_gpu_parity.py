@@ -142,6 +142,29 @@ def test_plan_rotated_and_shapes(F, orc, G, D):
         assert np.array_equal(pl.q_used.cpu().numpy()[p].view(np.uint32), rq.view(np.uint32))
 
 
+@pytest.mark.parametrize("G,D,mode,budget", [(1, 1, 0, 2), (2, 16, 0, 20), (5, 33, 0, 40), (8, 65, 0, 100),
+                                             (3, 127, 1, 16), (7, 100, 2, 3), (8, 128, 0, 48)])
+def test_plan_odd_shapes_bit_exact(F, orc, G, D, mode, budget):
+    """Plans at channel counts that leave lanes without a channel (D below
+    64, between 64 and 128) and head counts from 1 to 8, in the stored basis:
+    depths, level, scaled queries and active list equal the oracle's bit for
+    bit."""
+    P = 6
+    q, s2 = _plan_inputs(P, G, D, 31 * G + D)
+    say("plan odd shape", G, D, mode, budget)
+    pl = F.plan(dev(q), dev(s2), budget, mode)
+    depth, act, na = pl.depth.cpu().numpy(), pl.active.cpu().numpy(), pl.n_active.cpu().numpy()
+    th, qu = pl.theta.cpu().numpy(), pl.q_used.cpu().numpy()
+    for p in range(P):
+        rd, rth, rq = orc.plan(q[p], s2[p], budget, mode)
+        assert np.array_equal(depth[p], rd), p
+        assert th[p].view(np.uint32) == np.float32(rth).view(np.uint32)
+        assert np.array_equal(qu[p].view(np.uint32), rq.view(np.uint32))
+        nz = np.nonzero(rd)[0]
+        assert na[p] == nz.size
+        assert np.array_equal(act[p, :nz.size], nz) and np.all(act[p, nz.size:] == -1)
+
+
 SCAN_CASES = [  # (n, D, G, mode, budget)
     (4096, 128, 4, 0, 48), (4096 + 37, 128, 4, 0, 48), (1, 128, 4, 0, 48), (700, 128, 4, 0, 512),
     (700, 128, 4, 0, 0), (2000, 128, 4, 1, 32), (2000, 128, 4, 2, 2), (1500, 64, 8, 0, 92),
