@@ -16,15 +16,24 @@ constexpr int kSelThreads = 1024;
 // works for any multiple of 64 threads up to kSelThreads.
 constexpr int kSelectThreads = 512;
 constexpr int kBins = 2048;
-constexpr int kBuf = 4096;
 
-struct SelShared {
+// KB: capacity of buf, which holds the winners (k <= KB) and the bin a
+// radix level narrows a long source down to.  The full size serves every k
+// up to 4096; the small one (k <= 2048) takes 33 KB instead of 49 KB, so
+// four selection workgroups fit on a CU instead of three.
+template <int KB>
+struct SelSharedT {
+    static constexpr int kCap = KB;
     uint32_t hist[2][kBins];  // level l counts into hist[l & 1] and clears the other
-    uint64_t buf[kBuf + 8];   // + 8 zero pads after the winners for the linear rank loop
+    uint64_t buf[KB + 8];     // + 8 zero pads after the winners for the linear rank loop
     uint64_t wlo[kSelThreads / kWave], whi[kSelThreads / kWave];
     uint32_t nbuf;
     uint32_t bin, above, inbin;
 };
+using SelShared = SelSharedT<4096>;
+using SelSharedSmall = SelSharedT<2048>;
+// the threshold kernels count radix levels only and never fill buf
+using SelSharedHist = SelSharedT<8>;
 
 struct DenseSrc {
     const float* s;
@@ -85,7 +94,8 @@ struct Radix {
 };
 
 // Zeroes the first level's histogram (followed by a barrier).
-__device__ __forceinline__ Radix radix_start(int need, SelShared& sh)
+template <class SH>
+__device__ __forceinline__ Radix radix_start(int need, SH& sh)
 {
     for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh.hist[0][i] = 0;
     __syncthreads();
@@ -114,7 +124,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
 // Radix over offsets from the smallest element, `lo` (lo_t, hi_t: this
 // thread's extremes; ~0 and 0 when it holds none).  Zeroes the first
 // histogram.
-__device__ Radix radix_start_range(int need, uint64_t lo_t, uint64_t hi_t, SelShared& sh,
+template <class SH>
+__device__ Radix radix_start_range(int need, uint64_t lo_t, uint64_t hi_t, SH& sh,
                                    uint64_t& lo)
 {
 #pragma unroll
@@ -144,7 +155,8 @@ __device__ Radix radix_start_range(int need, uint64_t lo_t, uint64_t hi_t, SelSh
 
 // Histogram of the current level; the next level's buffer is zeroed here
 // (its last reader, the previous level's bin search, ended at a barrier).
-__device__ __forceinline__ uint32_t* level_begin(const Radix& r, SelShared& sh)
+template <class SH>
+__device__ __forceinline__ uint32_t* level_begin(const Radix& r, SH& sh)
 {
     uint32_t* nxt = sh.hist[(r.lvl + 1) & 1];
     for (int i = threadIdx.x; i < kBins; i += blockDim.x) nxt[i] = 0;
@@ -172,7 +184,8 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x)
 // sum over those groups names the group that holds the sought element, and
 // a second prefix sum over that group's 32 bins (one per lane) names the
 // bin.  Returns the number of elements in the bin.
-__device__ uint32_t level_end(Radix& r, SelShared& sh)
+template <class SH>
+__device__ uint32_t level_end(Radix& r, SH& sh)
 {
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -211,8 +224,8 @@ __device__ uint32_t level_end(Radix& r, SelShared& sh)
 
 // One radix level over src, four elements per thread loaded before any is
 // counted.
-template <class Src>
-__device__ uint32_t radix_level(const Src& src, Radix& r, SelShared& sh)
+template <class Src, class SH>
+__device__ uint32_t radix_level(const Src& src, Radix& r, SH& sh)
 {
     uint32_t* h = level_begin(r, sh);
     const int64_t bd = blockDim.x;
@@ -234,14 +247,14 @@ __device__ uint32_t radix_level(const Src& src, Radix& r, SelShared& sh)
 
 // Radix levels over src until the sought element's bin fits in LDS; that
 // bin is then copied to sh.buf and the remaining levels run there.
-template <class Src>
-__device__ Radix kth_largest(const Src& src, int need, SelShared& sh)
+template <class Src, class SH>
+__device__ Radix kth_largest(const Src& src, int need, SH& sh)
 {
     Radix r = radix_start(need, sh);
     uint32_t inbin;
     do {
         inbin = radix_level(src, r, sh);
-    } while (inbin > (uint32_t)kBuf && !r.done());
+    } while (inbin > (uint32_t)SH::kCap && !r.done());
     if (inbin <= 1) return r;
     if (threadIdx.x == 0) sh.nbuf = 0;
     __syncthreads();
@@ -250,7 +263,7 @@ __device__ Radix kth_largest(const Src& src, int need, SelShared& sh)
         const uint64_t v = src.get(e, ok);
         if (ok && r.in(v)) {
             const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
-            if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+            if (slot < (uint32_t)SH::kCap) sh.buf[slot] = v;
         }
     }
     __syncthreads();
@@ -259,20 +272,20 @@ __device__ Radix kth_largest(const Src& src, int need, SelShared& sh)
     return r;
 }
 
-// Up to kRegSlots candidates per thread held in registers: slot q of
-// thread t is candidate q * blockDim + t.
-constexpr int kRegSlots = 16;
-
+// Up to NS candidates per thread held in registers: slot q of thread t is
+// candidate q * blockDim + t.
+template <int NS>
 struct RegCands {
-    uint64_t v[kRegSlots];
+    uint64_t v[NS];
     uint32_t valid;  // bit q: slot q holds a candidate
 };
 
-__device__ __forceinline__ void load_regs(const uint64_t* c, int64_t cnt, RegCands& rc)
+template <int NS>
+__device__ __forceinline__ void load_regs(const uint64_t* c, int64_t cnt, RegCands<NS>& rc)
 {
     rc.valid = 0;
 #pragma unroll
-    for (int q = 0; q < kRegSlots; ++q) {
+    for (int q = 0; q < NS; ++q) {
         const int64_t e = (int64_t)q * blockDim.x + threadIdx.x;
         const bool ok = e < cnt;
         rc.v[q] = ok ? c[e] : 0;
@@ -282,18 +295,19 @@ __device__ __forceinline__ void load_regs(const uint64_t* c, int64_t cnt, RegCan
 
 // Radix levels over the candidates in registers, which are replaced by
 // their offsets from the smallest one (returned in `base`).
-__device__ Radix kth_largest_regs(RegCands& rc, int need, SelShared& sh, uint64_t& base)
+template <int NS, class SH>
+__device__ Radix kth_largest_regs(RegCands<NS>& rc, int need, SH& sh, uint64_t& base)
 {
     uint64_t lo = ~0ull, hi = 0;
 #pragma unroll
-    for (int q = 0; q < kRegSlots; ++q)
+    for (int q = 0; q < NS; ++q)
         if ((rc.valid >> q) & 1u) {
             lo = rc.v[q] < lo ? rc.v[q] : lo;
             hi = rc.v[q] > hi ? rc.v[q] : hi;
         }
     Radix r = radix_start_range(need, lo, hi, sh, base);
 #pragma unroll
-    for (int q = 0; q < kRegSlots; ++q) {
+    for (int q = 0; q < NS; ++q) {
         rc.v[q] -= base;
         // opaque to the optimiser: otherwise the winners' offset + base
         // folds back to the original value, which then stays live too
@@ -302,7 +316,7 @@ __device__ Radix kth_largest_regs(RegCands& rc, int need, SelShared& sh, uint64_
     for (;;) {
         uint32_t* h = level_begin(r, sh);
 #pragma unroll
-        for (int q = 0; q < kRegSlots; ++q)
+        for (int q = 0; q < NS; ++q)
             if (((rc.valid >> q) & 1u) && r.in(rc.v[q])) atomicAdd(&h[r.digit(rc.v[q])], 1u);
         if (level_end(r, sh) <= 1 || r.done()) break;
     }
@@ -313,13 +327,14 @@ __device__ Radix kth_largest_regs(RegCands& rc, int need, SelShared& sh, uint64_
 // per wavefront: the wavefront's winners are counted first, then each is
 // placed at the wavefront's base plus the winners before it (earlier slots,
 // then lower lanes of its own slot).
-__device__ __forceinline__ void winners_from_regs(const RegCands& rc, const Radix& r, uint64_t base,
-                                                  SelShared& sh)
+template <int NS, class SH>
+__device__ __forceinline__ void winners_from_regs(const RegCands<NS>& rc, const Radix& r, uint64_t base,
+                                                  SH& sh)
 {
     const int lane = lane_id();
     uint32_t wins = 0, total = 0;
 #pragma unroll
-    for (int q = 0; q < kRegSlots; ++q) {
+    for (int q = 0; q < NS; ++q) {
         const bool win = ((rc.valid >> q) & 1u) && r.at_or_above(rc.v[q]);
         wins |= win ? 1u << q : 0u;
         total += (uint32_t)__popcll(__ballot(win));
@@ -328,7 +343,7 @@ __device__ __forceinline__ void winners_from_regs(const RegCands& rc, const Radi
     if (lane == 0 && total != 0) slot = atomicAdd(&sh.nbuf, total);
     slot = (uint32_t)__shfl((int)slot, 0, kWave);
 #pragma unroll
-    for (int q = 0; q < kRegSlots; ++q) {
+    for (int q = 0; q < NS; ++q) {
         const bool win = (wins >> q) & 1u;
         const uint64_t b = __ballot(win);
         if (win) sh.buf[slot + (uint32_t)__popcll(b & lanes_below(lane))] = rc.v[q] + base;
@@ -397,15 +412,17 @@ __device__ __forceinline__ int count_above(const T* a, int nch, T x)
 // Exact top-k of one selection m, written to topk_idx / topk_val (by rank)
 // and sorted_idx (by token index): from its cnt candidates (cand, at most
 // cap), or, when `dense`, from its full score row (n tokens of npad).
+// NS: register slots per thread for the candidates; k <= SH::kCap.
+template <int NS = 16, class SH>
 __device__ void select_one(const float* __restrict__ srow, int64_t n, int64_t npad, bool dense,
                            const uint64_t* __restrict__ crow, int64_t cnt, int k, int64_t m,
                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_val,
-                           int32_t* __restrict__ sorted_idx, SelShared& sh)
+                           int32_t* __restrict__ sorted_idx, SH& sh)
 {
-    if (!dense && cnt <= (int64_t)kRegSlots * blockDim.x) {
+    if (!dense && cnt <= (int64_t)NS * blockDim.x) {
         // candidates read once into registers; the radix levels and the
         // winner gather run from there
-        RegCands rc;
+        RegCands<NS> rc;
         uint64_t base;
         load_regs(crow, cnt, rc);
         const Radix r = kth_largest_regs(rc, k, sh, base);
@@ -424,7 +441,7 @@ __device__ void select_one(const float* __restrict__ srow, int64_t n, int64_t np
             const uint64_t v = dense ? dsrc.get(e, ok) : csrc.get(e, ok);
             if (ok && r.at_or_above(v)) {
                 const uint32_t slot = atomicAdd(&sh.nbuf, 1u);
-                if (slot < (uint32_t)kBuf) sh.buf[slot] = v;
+                if (slot < (uint32_t)SH::kCap) sh.buf[slot] = v;
             }
         }
     }

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(const float* __r
                                                                 uint32_t* __restrict__ tau,
                                                                 uint32_t* __restrict__ counts)
 {
-    __shared__ SelShared sh;
+    __shared__ SelSharedHist sh;
     const int64_t m = blockIdx.x;
     if (threadIdx.x == 0) counts[m] = 0u;  // the selection's candidate count, for the filter that follows
     if (valid < k) {
@@ -107,22 +107,26 @@ __global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ s
     }
 }
 
-// Eight waves per SIMD: two workgroups per CU.  A selection whose
-// candidates overflowed their capacity, or number fewer than k, is selected
-// over its full score row when `scores` is given (top-k of materialised
-// scores); in the fused path (scores NULL) the repair kernel has selected it.
-__global__ __launch_bounds__(kSelectThreads, 6) void select_kernel(
+// A selection whose candidates overflowed their capacity, or number fewer
+// than k, is selected over its full score row when `scores` is given (top-k
+// of materialised scores); in the fused path (scores NULL) the repair
+// kernel has selected it.  SH, NS and WPE (waves per SIMD the registers
+// must allow) come in two forms: k <= 2048 with 8 register slots and the
+// small buffer, four workgroups per CU (stage 3 at 1M tokens x 288 pairs
+// 0.067 -> 0.063 ms); larger k with 16 slots and the full buffer, three.
+template <class SH, int NS, int WPE>
+__global__ __launch_bounds__(kSelectThreads, WPE) void select_kernel(
     const float* __restrict__ scores, int64_t n, int64_t npad, const uint32_t* __restrict__ counts,
     const uint64_t* __restrict__ cand, int64_t cap, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_val, int32_t* __restrict__ sorted_idx)
 {
-    __shared__ SelShared sh;
+    __shared__ SH sh;
     const int64_t m = blockIdx.x;
     const int64_t cnt = counts[m];
     const bool dense = cnt > cap || cnt < (int64_t)k;
     if (dense && !scores) return;
-    select_one(dense ? scores + m * npad : nullptr, n, npad, dense, cand + m * cap, cnt, k, m, topk_idx,
-               topk_val, sorted_idx, sh);
+    select_one<NS>(dense ? scores + m * npad : nullptr, n, npad, dense, cand + m * cap, cnt, k, m, topk_idx,
+                   topk_val, sorted_idx, sh);
 }
 
 // Union of the G winner lists of a pair, each sorted by token index: every
@@ -224,6 +228,18 @@ void launch_union(const int32_t* sorted, int P, int G, int k, int32_t* union_idx
     }
 }
 
+void launch_select(const float* scores, int64_t n, int64_t npad, const uint32_t* counts,
+                   const uint64_t* cand, int64_t cap, int k, int32_t* topk_idx, float* topk_val,
+                   int32_t* sorted, int64_t m, hipStream_t st)
+{
+    if (k <= SelSharedSmall::kCap)
+        select_kernel<SelSharedSmall, 8, 8><<<dim3((unsigned)m), kSelectThreads, 0, st>>>(
+            scores, n, npad, counts, cand, cap, k, topk_idx, topk_val, sorted);
+    else
+        select_kernel<SelShared, 16, 6><<<dim3((unsigned)m), kSelectThreads, 0, st>>>(
+            scores, n, npad, counts, cand, cap, k, topk_idx, topk_val, sorted);
+}
+
 }  // namespace
 
 TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows)
@@ -290,8 +306,7 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
                                                                            counts, cand, L.cap);
     }
     int32_t* sorted = (int32_t*)(w + L.off_sorted);
-    select_kernel<<<dim3((unsigned)L.m), kSelectThreads, 0, st>>>(scores, n, npad, counts, cand, L.cap,
-                                                              k, topk_idx, topk_val, sorted);
+    launch_select(scores, n, npad, counts, cand, L.cap, k, topk_idx, topk_val, sorted, L.m, st);
     launch_union(sorted, P, G, k, union_idx, union_len, st);
     return hipGetLastError();
 }
@@ -342,8 +357,7 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
         if ((e = launch_repair(base, P, G, k, counts, L.cap, repair, L.slots, topk_idx, topk_val, sorted,
                                st)) != hipSuccess)
             return e;
-        select_kernel<<<dim3((unsigned)L.m), kSelectThreads, 0, st>>>(nullptr, n, npad, counts, cand,
-                                                                  L.cap, k, topk_idx, topk_val, sorted);
+        launch_select(nullptr, n, npad, counts, cand, L.cap, k, topk_idx, topk_val, sorted, L.m, st);
         launch_union(sorted, P, G, k, union_idx, union_len, st);
     }
     return hipGetLastError();
