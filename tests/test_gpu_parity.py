@@ -239,6 +239,10 @@ TOPK_CASES = [  # (n, k, kind)
     (4096, 64, "normal"), (32768, 512, "normal"), (100000, 512, "ties"), (70, 70, "normal"),
     (1, 1, "normal"), (64 * 33 + 5, 200, "ties"), (20000, 4096, "normal"), (5000, 1, "ties"),
     (200000, 512, "allequal"), (131072, 2048, "normal"),
+    # both selection forms at their boundary (k <= 2048: 8 register slots and
+    # a 2048-entry winner buffer), with thousands of tied candidates
+    (150000, 2000, "ties"), (300000, 2048, "ties"), (60000, 2049, "ties"),
+    (200000, 2000, "coarse"),  # ~13k candidates tie at the cut: past the register slots
 ]
 
 
@@ -251,6 +255,8 @@ def test_topk_union_bit_exact(F, orc, n, k, kind):
     if kind == "ties":
         s = np.round(s * 3).astype(np.float32)
         s[..., ::5] = -0.0
+    if kind == "coarse":  # five or so distinct values: thousands tie at the k-th
+        s = np.round(s).astype(np.float32)
     if kind == "allequal":  # every score tied: candidates overflow -> dense path
         s[:] = 1.5
     s[..., n:] = -np.inf
