@@ -141,6 +141,17 @@ def test_long1m_step(F, orc):
     _check_properties(w, w.budget, 0, pl, scores, out)
     fused = F.scan_topk(planes, scales, w.n, pl, w.k)
     assert torch.equal(fused.idx, out.idx) and torch.equal(fused.union, out.union)
+    # the per-layer scope: calls over 8 and 16 of the pairs take other grids
+    # (fewer, larger workgroups per pair run one round) and must select the
+    # same winners as the one call over all 288
+    qd, s2d = torch.from_numpy(q).cuda(), torch.from_numpy(s2).cuda()
+    for lo, hi in ((0, 8), (280, 288), (16, 32)):
+        say("1M step, pairs", lo, "to", hi - 1, "in a call of their own")
+        pl_l = F.plan(qd[lo:hi], s2d[lo:hi], w.budget, 0)
+        part = F.scan_topk(planes[lo:hi], scales[lo:hi], w.n, pl_l, w.k)
+        assert torch.equal(part.idx, fused.idx[lo:hi]) and torch.equal(part.val, fused.val[lo:hi])
+        assert torch.equal(part.union, fused.union[lo:hi]) and torch.equal(part.union_len, fused.union_len[lo:hi])
+        del part
     del fused
     _compare_sampled(orc, w, [3, 150, 286], q, s2, w.budget, 0, planes, scales, pl, scores, out)
     del planes, scales, scores, out
