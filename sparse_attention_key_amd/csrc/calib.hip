@@ -112,6 +112,44 @@ __global__ __launch_bounds__(256) void cov_partial_kernel(const void* __restrict
             if (i0 + a < D && j0 + b < D) out[(size_t)(i0 + a) * D + j0 + b] = acc[a][b];
 }
 
+// Variances alone (no covariance asked for): partial[p][c][d] = the sum over
+// the chunk's tokens, in order, of (x_d - mu_d)^2 -- the float64 operations
+// of cov_partial_kernel's diagonal in the same order, so the variances equal
+// the covariance's diagonal bit for bit, at 1/D of its arithmetic.  One
+// thread per channel; a wavefront reads whole token rows.
+template <int DTYPE>
+__global__ __launch_bounds__(kMaxD) void var_partial_kernel(const void* __restrict__ keys, int64_t m,
+                                                            int D, int chunks,
+                                                            const double* __restrict__ mean,
+                                                            double* __restrict__ partial)
+{
+    const int p = blockIdx.y, c = blockIdx.x, d = threadIdx.x;
+    if (d >= D) return;
+    const int64_t t0 = (int64_t)c * kChunk;
+    const int64_t t1 = t0 + kChunk < m ? t0 + kChunk : m;
+    const double mu = mean[(size_t)p * D + d];
+    double acc = 0.0;
+#pragma unroll 8
+    for (int64_t t = t0; t < t1; ++t) {
+        const double x = key_at<DTYPE>(keys, ((size_t)p * m + t) * D + d) - mu;
+        acc = __builtin_fma(x, x, acc);
+    }
+    partial[((size_t)p * chunks + c) * D + d] = acc;
+}
+
+// var[p][d] = float((sum over chunks, in order) / m), as cov_reduce_kernel
+// forms the diagonal
+__global__ __launch_bounds__(kMaxD) void var_reduce_kernel(const double* __restrict__ partial, int64_t m,
+                                                           int D, int chunks, float* __restrict__ var)
+{
+    const int p = blockIdx.x;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        double s = 0.0;
+        for (int c = 0; c < chunks; ++c) s += partial[((size_t)p * chunks + c) * D + d];
+        var[(size_t)p * D + d] = (float)(s / (double)m);
+    }
+}
+
 // cov[p] = (sum over chunks, in order) / m; var[p][d] = float(cov[p][d][d])
 __global__ __launch_bounds__(256) void cov_reduce_kernel(const double* __restrict__ partial, int64_t m,
                                                          int D, int chunks, double* __restrict__ cov,
@@ -317,6 +355,21 @@ hipError_t launch_calib_covariance(const void* keys, int dtype, int P, int64_t m
     double* mpart = mean + (size_t)P * D;
     double* cpart = mpart + (size_t)P * chunks * D;
     const dim3 grid((unsigned)chunks, (unsigned)P);
+    if (!cov) {
+        // variances only: the mean, then the centred squares per channel
+        // (their partial sums reuse the mean's partial area)
+        if (dtype == 0) {
+            mean_partial_kernel<0><<<grid, 256, 0, st>>>(keys, m, D, chunks, mpart);
+            mean_reduce_kernel<<<dim3((unsigned)P), 128, 0, st>>>(mpart, m, D, chunks, mean);
+            var_partial_kernel<0><<<grid, kMaxD, 0, st>>>(keys, m, D, chunks, mean, mpart);
+        } else {
+            mean_partial_kernel<1><<<grid, 256, 0, st>>>(keys, m, D, chunks, mpart);
+            mean_reduce_kernel<<<dim3((unsigned)P), 128, 0, st>>>(mpart, m, D, chunks, mean);
+            var_partial_kernel<1><<<grid, kMaxD, 0, st>>>(keys, m, D, chunks, mean, mpart);
+        }
+        var_reduce_kernel<<<dim3((unsigned)P), kMaxD, 0, st>>>(mpart, m, D, chunks, var);
+        return hipGetLastError();
+    }
     if (dtype == 0) {
         mean_partial_kernel<0><<<grid, 256, 0, st>>>(keys, m, D, chunks, mpart);
         mean_reduce_kernel<<<dim3((unsigned)P), 128, 0, st>>>(mpart, m, D, chunks, mean);

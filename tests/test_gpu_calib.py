@@ -30,17 +30,20 @@ COV_CASES = [("klt_sample", 8192, 128), ("offset_ragged", 5000, 128), ("m1", 1, 
              ("d64", 2049, 64)]
 
 
-@pytest.mark.parametrize("case,m,D", COV_CASES)
-def test_covariance_matches_definition(F, orc, case, m, D):
-    P = 3
+def _cov_keys(case, m, D, P=3):
     g = np.random.default_rng(m * 131 + D)
     if case == "klt_sample":
         w = wl.WORKLOADS["host1m_klt"]
         xs = np.stack([wl.calibration_sample(w, p) for p in range(P)])
-        keys = bf16_dev(xs)
-    else:
-        xs = (g.standard_normal((P, m, D)) * np.exp(0.8 * g.standard_normal(D)) + 7.0).astype(np.float32)
-        keys = dev(xs)
+        return xs, bf16_dev(xs)
+    xs = (g.standard_normal((P, m, D)) * np.exp(0.8 * g.standard_normal(D)) + 7.0).astype(np.float32)
+    return xs, dev(xs)
+
+
+@pytest.mark.parametrize("case,m,D", COV_CASES)
+def test_covariance_matches_definition(F, orc, case, m, D):
+    P = 3
+    xs, keys = _cov_keys(case, m, D, P)
     say("calib covariance", case, P, m, D)
     cov, var = F.calib_covariance(keys)
     cov, var = cov.cpu().numpy(), var.cpu().numpy()
@@ -51,6 +54,19 @@ def test_covariance_matches_definition(F, orc, case, m, D):
         rv = orc.calib.channel_variance(xs[p])
         # the same float64 value up to summation order, rounded once to float32
         assert np.all(np.abs(var[p].astype(np.float64) - rv) <= np.spacing(np.abs(rv)) + 1e-30), p
+
+
+@pytest.mark.parametrize("case,m,D", COV_CASES)
+def test_variances_alone_equal_the_covariance_diagonal(F, case, m, D):
+    """Asked for variances only, the library skips the covariance and sums
+    the centred squares per channel in the covariance diagonal's own order:
+    the variances must equal those of the full call bit for bit."""
+    _, keys = _cov_keys(case, m, D)
+    say("calib variances alone", case, m, D)
+    _, var_full = F.calib_covariance(keys)
+    cov, var_only = F.calib_covariance(keys, with_cov=False)
+    assert cov is None
+    assert torch.equal(var_only.view(torch.int32), var_full.view(torch.int32))
 
 
 def _basis_checks(U, lam, C, ref_U, ref_lam):
