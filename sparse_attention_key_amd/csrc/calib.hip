@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256) void mean_partial_kernel(const void* __restric
         const int d = d0 + (threadIdx.x & 127), half = threadIdx.x >> 7;
         double acc = 0.0;
         if (d < D)
+#pragma unroll 8
             for (int64_t t = t0 + half; t < t1; t += 2) acc += key_at<DTYPE>(keys, ((size_t)p * m + t) * D + d);
         s_part[threadIdx.x] = acc;
         __syncthreads();
