@@ -225,6 +225,15 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
  * at once, and any further ones by one workgroup per row in turn, so the
  * workspace does not grow with the number of failures (at 1M tokens x 288
  * pairs, G = 4, k = 512 it is about 0.9 GB).
+ *
+ * An index in host memory (hipHostMalloc'd and mapped, read over the host
+ * link; the call asks the HIP runtime what kind of memory `planes` is) is
+ * read once per call instead of the sampled runs twice: the sample stage
+ * keeps every score it computes in the workspace, and the filter pass skips
+ * the sampled runs and keeps their stored scores that reach the threshold
+ * instead.  This needs the larger of the two workspace layouts, which
+ * fathom_scan_topk_workspace_bytes() always returns; a smaller workspace
+ * that fits the device layout gives the same results without the staging.
  *   ws  device workspace of at least fathom_scan_topk_workspace_bytes().
  * Errors: as fathom_scan and fathom_topk.
  */
@@ -242,7 +251,9 @@ int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int32_t P, 
  * is exactly fathom_scan_topk.
  *   stage 1: sample scores and per-head thresholds (written into ws)
  *   stage 2: the scan over every block with the threshold filter -- one
- *            kernel launch, the step's dominant kernel
+ *            kernel launch, the step's dominant kernel (for an index in
+ *            host memory: over every block outside the sample, then a
+ *            second launch filters the sample's stored scores)
  *   stage 3: overflow repair, exact selection and union (the outputs; they
  *            may be NULL in stages 1 and 2)
  * Errors: ERR_ARG for a stage outside 1..3, else as fathom_scan_topk.

@@ -189,7 +189,25 @@ int fathom_topk(const float* scores, int32_t P, int32_t G, int64_t n, int32_t k,
 size_t fathom_scan_topk_workspace_bytes(int32_t P, int32_t G, int64_t n, int32_t k)
 {
     if (P < 1 || G < 1 || G > kMaxG || n < 1 || k < 1 || k > n || k > kMaxK) return 0;
-    return topk_layout(P, G, n, k).bytes_fused;
+    // enough for either layout: an index in device memory, or one read over the host link
+    const size_t dev = topk_layout(P, G, n, k).bytes_fused;
+    const size_t host = topk_layout(P, G, n, k, kRepairSlots, true).bytes_fused;
+    return dev > host ? dev : host;
+}
+
+// Whether the scan reads this index over the host link (memory the HIP
+// runtime knows as host memory, e.g. hipHostMalloc'd and mapped).  An
+// address the runtime does not know is taken as device memory, and the
+// error that query leaves is cleared so that a later launch check does not
+// report it.
+static bool host_resident(const void* p)
+{
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return at.type == hipMemoryTypeHost;
 }
 
 // Argument checks shared by the fused entry points; fills the scan's
@@ -243,7 +261,13 @@ static int scan_topk_impl(const uint64_t* planes, const uint16_t* scales, int32_
     const int s = scan_topk_check(planes, scales, P, D, n, nb_cap, depth, active, n_active, q_used, G, k,
                                   topk_idx, topk_val, union_idx, union_len, stages, a);
     if (s) return s;
-    const TopkLayout L = topk_layout(P, G, n, k);
+    // over the host link, the sample's scores are kept for stage 2 when the
+    // workspace holds them (the results are the same either way)
+    TopkLayout L = topk_layout(P, G, n, k);
+    if (host_resident(planes)) {
+        const TopkLayout Ls = topk_layout(P, G, n, k, kRepairSlots, true);
+        if (ws && ws_bytes >= Ls.bytes_fused) L = Ls;
+    }
     if (!ws || ws_bytes < L.bytes_fused) return FATHOM_ERR_WORKSPACE;
     if (!aligned16(ws)) return FATHOM_ERR_ALIGN;
     return hip_status(launch_scan_topk(a, P, G, k, topk_idx, topk_val, union_idx, union_len, ws, L,
@@ -289,6 +313,10 @@ int fathom_scan_topk_noalloc(const uint64_t* planes, const uint16_t* scales, int
     TopkLayout L = topk_layout(P, G, n, k, rows);
     while (L.bytes_fused > kScratchBytes && rows > 1) L = topk_layout(P, G, n, k, --rows);
     if (L.bytes_fused > kScratchBytes) return FATHOM_ERR_WORKSPACE;
+    if (host_resident(planes)) {  // the staged sample, where the scratch holds it
+        const TopkLayout Ls = topk_layout(P, G, n, k, rows, true);
+        if (Ls.bytes_fused <= kScratchBytes) L = Ls;
+    }
     void* ws = nullptr;
     if ((s = scratch_address(&ws)) != FATHOM_OK) return s;
     return hip_status(launch_scan_topk(a, P, G, k, topk_idx, topk_val, union_idx, union_len, ws, L, 7,

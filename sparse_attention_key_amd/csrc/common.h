@@ -125,8 +125,11 @@ struct ScanArgs {
     const int32_t* n_active;
     const float* q_used;
     int64_t stride;        // 1, or: scan one run of 32 consecutive blocks in every stride runs
+    int64_t skip;          // 0, or a power of two s >= 2: the runs the sample took (one in every s,
+                           // the first included) are neither read nor filtered
     int64_t nlb;           // logical blocks per pair (rows of the STORE output / 64)
     float* out;            // STORE: [P][G][nlb * 64]; LANEMAX: [P][G][nlb * 4] (maxima of 16 tokens)
+    float* out2;           // LANEMAX, or null: every score as well ([P][G][nlb * 64], as STORE)
     const uint32_t* tau;   // FILTER: [P][G] key thresholds
     uint32_t* counts;      // FILTER: [P][G]
     uint64_t* cand;        // FILTER: [P][G][cap]
@@ -156,13 +159,20 @@ struct TopkLayout {
     int64_t sample_nlb;  // logical sample blocks per pair (whole runs)
     int64_t cap;         // candidate capacity per selection
     bool lanemax;        // fused threshold from per-lane maxima of the sample
+    bool staged;         // fused: the sample stores every score it reads, and stage 2 filters
+                         // those stored scores instead of reading the sampled runs again
     int rank;            // fused threshold: this order statistic of the sample
     size_t off_tau, off_count, off_cand, off_sorted, bytes;  // top-k from given scores
     int slots;           // fused: full score rows (pairs) for the repair, reused in turn
-    size_t off_sample, off_repair, bytes_fused;  // fused scan + top-k
+    size_t off_scores;   // staged: the sample's scores (the sample itself when it holds every score)
+    size_t off_sample, off_repair, bytes_fused;  // fused scan + top-k (the sample, used by
+                                                 // stages 1-2, and the repair rows, used by
+                                                 // stage 3, share their memory)
 };
-// rows: repair rows of the fused path, at most this many (and at most P)
-TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows = kRepairSlots);
+// rows: repair rows of the fused path, at most this many (and at most P);
+// staged: the layout for an index the scan reads over the host link (taken
+// only when the sample stride is at least 2)
+TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows = kRepairSlots, bool staged = false);
 hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int32_t* topk_idx,
                        float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
                        const TopkLayout& L, hipStream_t st);

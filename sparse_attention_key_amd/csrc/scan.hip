@@ -191,7 +191,7 @@ __device__ __forceinline__ int wave_max_dpp(int v)
 // Tile `tile` of pair p: logical blocks tile * gb .. tile * gb + gb - 1.
 // STORE and LANEMAX write row `op` of the output (the pair itself, or a
 // repair row).
-template <int GR, int MODE, int C>
+template <int GR, int MODE, int C, bool STG>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const int G, const int A,
                                           const int tile, const int op, const PairTables<GR>& T,
                                           unsigned char* code, unsigned char* coef, v4i* stage)
@@ -205,7 +205,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     // block indices fit 32 bits (the host caps n below 2^31 tokens), and the
     // plane and scale offsets below fit 31 bits (the host rejects a pair whose
     // plane rows span 2^31 bytes or more)
-    const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride;
+    const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride, skip = (int)a.skip;
     // Iteration i of wavefront w takes logical blocks lg0 + i IB + w NB + (0 .. NB-1):
     // at any time the four wavefronts of a workgroup read neighbouring blocks,
     // so each 128-byte line of a plane row is used by all of them at once.
@@ -373,6 +373,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     // The NB blocks of an iteration lie in one run, so they are consecutive;
     // blocks past the index read as zeros (the buffer bound) and are masked.
     auto phys = [&](int lb) { return __builtin_amdgcn_readfirstlane((lb / kRun) * kRun * stride + (lb % kRun)); };
+    // a physical block in a run that the sample stage took (staged filter: not read, no candidates)
+    auto sampled = [&](int pb) { return STG && MODE == kFilter && ((pb / kRun) & (skip - 1)) == 0; };
     // per-lane offset of plane s of step u; a plane the slot does not read
     // gets bit 31 set, which is out of range (kept in vector registers: a
     // per-plane lane mask would take scalar registers for the whole loop)
@@ -453,13 +455,14 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
     {
         const int pb0 = phys(lb0);
         mask_dead(pb0);
-        const __amdgpu_buffer_rsrc_t r = plane_rsrc(pb0, true);
+        const bool live0 = !sampled(pb0);
+        const __amdgpu_buffer_rsrc_t r = plane_rsrc(pb0, live0);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 w[u][s] = __builtin_amdgcn_raw_buffer_load_b32(r, voff(u, s), (int)(s * ldb8), 0);
-        issue_scales(pb0, true, sc);
+        issue_scales(pb0, live0, sc);
     }
     for (; lb0 < lgend; lb0 += IB) {
         const int lbn = lb0 + IB;
@@ -469,7 +472,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int64_t left = a.n - (int64_t)(pb0 + b) * 64;
-            nval[b] = (lb0 + b < nlb && pb0 + b < nbk) ? (int)(left < 64 ? left : 64) : 0;
+            nval[b] = (lb0 + b < nlb && pb0 + b < nbk && !sampled(pb0)) ? (int)(left < 64 ? left : 64) : 0;
         }
 
         // ---- block exponents: largest exponent field of the read scales (>= 1);
@@ -510,11 +513,11 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                 }
             }
         }
-        issue_scales(pbn, more, sc);
+        issue_scales(pbn, more && !sampled(pbn), sc);
         // ---- codes to LDS (a step with no slot to read writes nothing: its
         // stale records meet zero coefficients)
         if (more) mask_dead(pbn);
-        const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pbn, more);
+        const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pbn, more && !sampled(pbn));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             // the step's depth as a fresh scalar each iteration, so its
@@ -602,7 +605,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                     }
                 }
             } else {
-                if (MODE == kStore) {
+                if (MODE == kStore || STG) {  // every score (LANEMAX, staged: into the second output)
+                    float* const so = MODE == kStore ? a.out : a.out2;
 #pragma unroll
                     for (int rho = 0; rho < 4; ++rho) {
                         const bool tval = toff[rho] < nval[b];
@@ -611,11 +615,12 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
                             const int h = kap + 4 * gr;
                             const float sc = exact_score(o[rho][gr], recombine(kk[gr]), rho, Eb[b] - 1 - sig[gr]);
                             if (h < G && lb < nlb)
-                                a.out[((size_t)op * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
+                                so[((size_t)op * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
                                     tval ? sc : -INFINITY;
                         }
                     }
-                } else {
+                }
+                if (MODE == kLaneMax) {
                     // Maxima of 16 tokens from the top two digit rows (S ~ 2^(17-rho)
                     // hi + K): the sample is only a statistic for the threshold, whose
                     // exactness the candidate count check keeps, so an estimate
@@ -656,7 +661,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 // quarters are about equally deep (fixed-depth plans, and A > 64), and loses
 // to the per-wavefront form when the deep slots sit in one quarter (the
 // others wait for it at the barrier).
-template <int GR, int MODE, int C>
+template <int GR, int MODE, int C, bool STG>
 __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p, const int G, const int A,
                                           const int tile, const int op, const PairTables<GR>& T,
                                           unsigned char* code0, unsigned char* code, unsigned char* coef,
@@ -671,7 +676,7 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
     // block indices fit 32 bits (the host caps n below 2^31 tokens), and the
     // plane and scale offsets below fit 31 bits (the host rejects a pair whose
     // plane rows span 2^31 bytes or more)
-    const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride;
+    const int nlb = (int)a.nlb, nbk = (int)a.nb, stride = (int)a.stride, skip = (int)a.skip;
     // Iteration i of the workgroup reads the plane words of logical blocks
     // lg0 + i IB .. lg0 + i IB + IB - 1 (each wavefront its own slots), and
     // wavefront w multiplies and scores blocks lg0 + i IB + w NB + (0 .. NB-1).
@@ -850,6 +855,8 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
     // The NB blocks of an iteration lie in one run, so they are consecutive;
     // blocks past the index read as zeros (the buffer bound) and are masked.
     auto phys = [&](int lb) { return __builtin_amdgcn_readfirstlane((lb / kRun) * kRun * stride + (lb % kRun)); };
+    // a physical block in a run that the sample stage took (staged filter: not read, no candidates)
+    auto sampled = [&](int pb) { return STG && MODE == kFilter && ((pb / kRun) & (skip - 1)) == 0; };
     // per-lane offset of plane s of the lane's row segment; a plane the slot
     // does not read gets bit 31 set, which is out of range (kept in vector
     // registers: a per-plane lane mask would take scalar registers for the
@@ -963,10 +970,11 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
     {
         const int pw0 = phys(lg0);
         mask_dead(pw0);
-        const __amdgpu_buffer_rsrc_t r = plane_rsrc(pw0, true);
+        const bool live0 = !sampled(pw0);
+        const __amdgpu_buffer_rsrc_t r = plane_rsrc(pw0, live0);
 #pragma unroll
         for (int s = 0; s < 4; ++s) w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, vo[s], 0, 0));
-        issue_scales(phys(lg0 + wave * NB), true, sc);
+        issue_scales(phys(lg0 + wave * NB), live0, sc);
     }
     for (int lw0 = lg0; lw0 < lgend; lw0 += IB) {
         const int lb0 = lw0 + wave * NB;  // this wavefront's blocks (products, scales, outputs)
@@ -978,7 +986,7 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int64_t left = a.n - (int64_t)(pb0 + b) * 64;
-            nval[b] = (lb0 + b < nlb && pb0 + b < nbk) ? (int)(left < 64 ? left : 64) : 0;
+            nval[b] = (lb0 + b < nlb && pb0 + b < nbk && !sampled(pb0)) ? (int)(left < 64 ? left : 64) : 0;
         }
 
         // ---- block exponents: largest exponent field of the read scales (>= 1);
@@ -1019,7 +1027,7 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
                 }
             }
         }
-        issue_scales(pbn, more, sc);
+        issue_scales(pbn, more && !sampled(pbn), sc);
         // ---- codes to LDS, then the next iteration's plane words
         if (tail) fix_shift(w);
         if (wq == 0) __builtin_amdgcn_s_setprio(3);  // the deepest slots: the others wait on it
@@ -1027,7 +1035,7 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
         shifted = false;
         if (more) mask_dead(pwn);
         {
-            const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pwn, more);
+            const __amdgpu_buffer_rsrc_t rn = plane_rsrc(pwn, more && !sampled(pwn));
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rn, vo[s], 0, 0));
@@ -1098,7 +1106,8 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
                     }
                 }
             } else {
-                if (MODE == kStore) {
+                if (MODE == kStore || STG) {  // every score (LANEMAX, staged: into the second output)
+                    float* const so = MODE == kStore ? a.out : a.out2;
 #pragma unroll
                     for (int rho = 0; rho < 4; ++rho) {
                         const bool tval = toff[rho] < nval[b];
@@ -1107,11 +1116,12 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
                             const int h = kap + 4 * gr;
                             const float sc = exact_score(o[rho][gr], recombine(kk[gr]), rho, Eb[b] - 1 - sig[gr]);
                             if (h < G && lb < nlb)
-                                a.out[((size_t)op * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
+                                so[((size_t)op * G + h) * (a.nlb * 64) + (int64_t)lb * 64 + toff[rho]] =
                                     tval ? sc : -INFINITY;
                         }
                     }
-                } else {
+                }
+                if (MODE == kLaneMax) {
                     // Maxima of 16 tokens from the top two digit rows (S ~ 2^(17-rho)
                     // hi + K): the sample is only a statistic for the threshold, whose
                     // exactness the candidate count check keeps, so an estimate
@@ -1145,7 +1155,7 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
     if (MODE == kFilter && scnt) flush();
 }
 
-template <int GR, int MODE>
+template <int GR, int MODE, bool STG>
 __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const int G, const int tile,
                                           const int op)
 {
@@ -1243,20 +1253,22 @@ __device__ __forceinline__ void scan_pair(const ScanArgs& a, const int p, const 
     const int C = A <= 32 ? 1 : A <= 64 ? 2 : 4;
     const bool shared = C == 4 || (T.slot[0] >> 8) == (T.slot[24 * C] >> 8);
     if (shared) {
-        if (C == 1) scan_body_shared<GR, MODE, 1>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
-        else if (C == 2) scan_body_shared<GR, MODE, 2>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
-        else scan_body_shared<GR, MODE, 4>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
+        if (C == 1) scan_body_shared<GR, MODE, 1, STG>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
+        else if (C == 2) scan_body_shared<GR, MODE, 2, STG>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
+        else scan_body_shared<GR, MODE, 4, STG>(a, p, G, A, tile, op, T, s_code[0], code, coef, stage);
     } else {
-        if (C == 1) scan_body<GR, MODE, 1>(a, p, G, A, tile, op, T, code, coef, stage);
-        else scan_body<GR, MODE, 2>(a, p, G, A, tile, op, T, code, coef, stage);
+        if (C == 1) scan_body<GR, MODE, 1, STG>(a, p, G, A, tile, op, T, code, coef, stage);
+        else scan_body<GR, MODE, 2, STG>(a, p, G, A, tile, op, T, code, coef, stage);
     }
 }
 
 // blockIdx.y is the pair, blockIdx.x its tile of gb logical blocks.
-template <int GR, int MODE>
+// STG: FILTER skips the runs the sample took (a.skip); LANEMAX also
+// writes every score of the sample to a.out2.
+template <int GR, int MODE, bool STG>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a, int G)
 {
-    scan_pair<GR, MODE>(a, (int)blockIdx.y, G, (int)blockIdx.x, (int)blockIdx.y);
+    scan_pair<GR, MODE, STG>(a, (int)blockIdx.y, G, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // Fused path, stage 3: the heads whose candidate list failed (more than
@@ -1313,7 +1325,7 @@ __global__ __launch_bounds__(kThreads) void repair_scan_kernel(ScanArgs a, int P
 {
     const int fp = nth_failed_pair(counts, P, G, cap, k, blockIdx.y);
     if (fp < 0) return;
-    scan_pair<GR, kStore>(a, fp, G, (int)blockIdx.x, (int)blockIdx.y);
+    scan_pair<GR, kStore, false>(a, fp, G, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // (2) Workgroup r selects the failed heads of failed pair r from row r
@@ -1335,7 +1347,7 @@ __global__ __launch_bounds__(kThreads) void repair_select_kernel(ScanArgs a, int
         const int fp = nth_failed_pair(counts, P, G, cap, k, i);
         if (fp < 0) break;
         if (i >= gridDim.x) {
-            scan_pair<GR, kStore>(a, fp, G, 0, (int)blockIdx.x);  // one tile: a.gb covers the pair
+            scan_pair<GR, kStore, false>(a, fp, G, 0, (int)blockIdx.x);  // one tile: a.gb covers the pair
             __syncthreads();  // the row is complete (and the pair's LDS tables free)
         }
         for (int h = 0; h < G; ++h) {
@@ -1354,7 +1366,7 @@ hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
     ScanArgs a = args;
     const int rows = P;
     // blocks per workgroup: 1024, or fewer (a multiple of every iteration's
-    // 16 blocks, at least 64) while the grid has fewer workgroups than
+    // 16 blocks, at least 64, or 32 for the staged sample) while the grid has fewer workgroups than
     // `target`.  Long ranges spread each workgroup's start-up (the pair's
     // tables, the first loads, the last flush) over more blocks: at 1M
     // tokens x 288 pairs the filtered scan takes 1.10 ms with 256 blocks per
@@ -1367,12 +1379,22 @@ hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
     // filter in 0.19 ms against 0.22 for 576 of 1024.  The sampled stage
     // reads one run in 16, so its workgroups are short and more of them
     // (2048) keep the chip busy: 0.105 ms at 288 pairs against 0.125 with 512.
-    const int64_t target = MODE == kLaneMax || rows >= 64 ? 2048 : 512;
+    // The staged sample of an index read over the host link (a.out2 set)
+    // wants the shortest workgroups, 32 blocks: 3.95 ms at 1M tokens x 288
+    // pairs against 4.08 with 64, 4.25 with 256 and 4.42 with 128.
+    const bool host_sample = MODE == kLaneMax && a.out2 != nullptr;
+    const int64_t target = host_sample ? 8192 : MODE == kLaneMax || rows >= 64 ? 2048 : 512;
     a.gb = kGroupBlocks;
-    while (a.gb > 64 && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < target) a.gb /= 2;
+    while (a.gb > (host_sample ? 32 : 64) && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < target) a.gb /= 2;
     dim3 grid((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)rows);
-    if (G <= 4) scan_kernel<1, MODE><<<grid, kThreads, 0, st>>>(a, G);
-    else scan_kernel<2, MODE><<<grid, kThreads, 0, st>>>(a, G);
+    const bool stg = (MODE == kFilter && a.skip != 0) || (MODE == kLaneMax && a.out2 != nullptr);
+    if (MODE != kStore && stg) {
+        if (G <= 4) scan_kernel<1, MODE, MODE != kStore><<<grid, kThreads, 0, st>>>(a, G);
+        else scan_kernel<2, MODE, MODE != kStore><<<grid, kThreads, 0, st>>>(a, G);
+    } else {
+        if (G <= 4) scan_kernel<1, MODE, false><<<grid, kThreads, 0, st>>>(a, G);
+        else scan_kernel<2, MODE, false><<<grid, kThreads, 0, st>>>(a, G);
+    }
     return hipGetLastError();
 }
 

@@ -291,7 +291,7 @@ void launch_select(const float* scores, int64_t n, int64_t npad, const uint32_t*
 
 }  // namespace
 
-TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows)
+TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows, bool staged)
 {
     TopkLayout L{};
     const int64_t nb = (n + 63) / 64;
@@ -303,6 +303,7 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows)
     L.stride = s;
     // maxima of groups of 16 tokens (four per block) carry almost the same
     // tail information as the tokens themselves once there are >= 8k of them
+    L.staged = staged && s >= 2;
     L.lanemax = n >= 128 * (int64_t)k * s;
     // the fused threshold is the rank-th largest sample value: with one run
     // in every s sampled, about rank * s >= 2k scores lie above it.  That is
@@ -321,8 +322,15 @@ TopkLayout topk_layout(int P, int G, int64_t n, int k, int rows)
     L.bytes = L.off_sorted + (size_t)L.m * (size_t)k * 4;
     // the sample: per-lane maxima (4 per block) or every score (64 per block)
     L.off_sample = up(L.bytes);
-    L.off_repair = up(L.off_sample + (size_t)L.m * (size_t)L.sample_nlb * (L.lanemax ? 4 : 64) * 4);
-    L.bytes_fused = L.off_repair + (size_t)L.slots * (size_t)G * (size_t)nb * 64 * 4;
+    L.off_repair = L.off_sample;
+    size_t sample_bytes = (size_t)L.m * (size_t)L.sample_nlb * (L.lanemax ? 4 : 64) * 4;
+    L.off_scores = L.off_sample;
+    if (L.staged && L.lanemax) {  // the maxima set the threshold; every score is kept beside them
+        L.off_scores = up(L.off_sample + sample_bytes);
+        sample_bytes = L.off_scores - L.off_sample + (size_t)L.m * (size_t)L.sample_nlb * 64 * 4;
+    }
+    const size_t repair_bytes = (size_t)L.slots * (size_t)G * (size_t)nb * 64 * 4;
+    L.bytes_fused = L.off_sample + (sample_bytes > repair_bytes ? sample_bytes : repair_bytes);
     return L;
 }
 
@@ -360,6 +368,43 @@ hipError_t launch_topk(const float* scores, int P, int G, int64_t n, int k, int3
     return hipGetLastError();
 }
 
+// Fused path, stage 2, staged sample: the scores that stage 1 stored for
+// the sampled runs (row m: [sample_nlb * 64], tokens past n and blocks past
+// the index at -inf) are kept where they reach their selection's threshold,
+// as the filtered scan keeps its own candidates (same keys, same capacity
+// rule).  Grid: (selection m, chunks of its row).
+__global__ __launch_bounds__(256) void sample_filter_kernel(const float* __restrict__ sample, int64_t row,
+                                                            int64_t n, int64_t stride,
+                                                            const uint32_t* __restrict__ tau,
+                                                            uint32_t* __restrict__ counts,
+                                                            uint64_t* __restrict__ cand, int64_t cap)
+{
+    const int64_t m = blockIdx.x;
+    const uint32_t tk = tau[m];
+    const float th = tk <= 0x007FFFFFu ? -INFINITY : key_score(tk);
+    const float* r = sample + m * row;
+    const int lane = lane_id();
+    for (int64_t e0 = (int64_t)blockIdx.y * blockDim.x; e0 < row; e0 += (int64_t)gridDim.y * blockDim.x) {
+        const int64_t e = e0 + threadIdx.x;
+        bool keep = false;
+        float sc = 0.0f;
+        int64_t tok = 0;
+        if (e < row) {
+            const int64_t lb = e >> 6;  // logical sample block: run lb / 32, one in every stride
+            tok = ((lb >> 5) * stride * 32 + (lb & 31)) * 64 + (e & 63);
+            sc = r[e];
+            keep = tok < n && sc >= th;
+        }
+        const uint64_t b = __ballot(keep);
+        if (!b) continue;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&counts[m], (uint32_t)__popcll(b));
+        base = (uint32_t)__shfl((int)base, 0, kWave);
+        const uint32_t pos = base + (uint32_t)__popcll(b & lanes_below(lane));
+        if (keep && (int64_t)pos < cap) cand[m * cap + pos] = composite(score_key(sc), (uint32_t)tok);
+    }
+}
+
 hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* topk_idx,
                             float* topk_val, int32_t* union_idx, int32_t* union_len, void* ws,
                             const TopkLayout& L, int stages, hipStream_t st)
@@ -376,10 +421,12 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
 
     if (stages & 1) {
         // threshold: scores of every stride-th block, exact k-th largest (the
-        // threshold kernel also clears the candidate counts)
+        // threshold kernel also clears the candidate counts).  Staged, the
+        // sample keeps every score it computes for stage 2.
         a.stride = L.stride;
         a.nlb = L.sample_nlb;
         a.out = sample;
+        a.out2 = L.staged && L.lanemax ? (float*)(w + L.off_scores) : nullptr;
         if ((e = launch_scan_args(a, P, G, L.lanemax ? 2 : 0, st)) != hipSuccess) return e;
         // every lane maximum is a distinct token's score, so the k-th largest
         // of them is still a lower bound of the k-th largest score
@@ -388,15 +435,24 @@ hipError_t launch_scan_topk(const ScanArgs& base, int P, int G, int k, int32_t* 
                                                                      L.rank, tau, counts);
     }
     if (stages & 2) {
-        // filter: every block, keeping the scores at or above the threshold
+        // filter: every block, keeping the scores at or above the threshold.
+        // Staged, the sampled runs are not read again: their stored scores
+        // are filtered instead, so every index byte crosses the link once.
         a = base;
         a.stride = 1;
+        a.skip = L.staged ? L.stride : 0;
         a.nlb = nb;
         a.tau = tau;
         a.counts = counts;
         a.cand = cand;
         a.cap = L.cap;
         if ((e = launch_scan_args(a, P, G, 1, st)) != hipSuccess) return e;
+        if (L.staged) {
+            const int64_t row = L.sample_nlb * 64;
+            const int64_t chunks = (row + 4095) / 4096;  // 16 scores per thread
+            sample_filter_kernel<<<dim3((unsigned)L.m, (unsigned)(chunks < 65535 ? chunks : 65535)), 256, 0, st>>>(
+                (const float*)(w + L.off_scores), row, n, L.stride, tau, counts, cand, L.cap);
+        }
     }
     if (stages & 4) {
         // selections whose candidates failed (overflow, or fewer than k):

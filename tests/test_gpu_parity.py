@@ -555,6 +555,51 @@ def test_host_resident_index_matches_device(F, orc):
     sh.free()
 
 
+@pytest.mark.parametrize("k", [64, 512])
+def test_host_resident_staged_sample(F, orc, k):
+    """Over the host link the sample stage keeps its scores and the filter
+    skips the sampled runs (every index byte read once).  At n = 600,013 the
+    sample is one run in 32 for k = 64 (group maxima set the threshold, the
+    scores are stored beside them) and one run in 16 for k = 512 (every
+    sampled score, which are also the stored ones).  One call, the three stages
+    called one by one, and the same step from HBM must all give the same
+    winners, values and unions, equal to the oracle's."""
+    import torch
+
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    w = wl.WORKLOADS["host1m_klt"]
+    P, n = 3, 600000 + 13
+    s = _sample_stride(n, k)
+    assert s == (32 if k == 64 else 16) and (n >= 128 * k * s) == (k == 64)
+    xs = [wl.keys_host(w, p, n=n) for p in range(P)]
+    qs = np.stack([wl.queries(w, p) for p in range(P)])
+    rots, lams = zip(*[orc.calib.klt_basis(wl.calibration_sample(w, p)) for p in range(P)])
+    rot, lam = np.stack(rots), np.stack(lams)
+    say("host-resident staged sample", n, k)
+    planes, scales = F.pack(bf16_dev(np.stack(xs)), rot=dev(rot))
+    ph = PinnedHost(planes.numel() * 8)
+    sh = PinnedHost(scales.numel() * 2)
+    st = torch.cuda.current_stream()
+    ph.copy_from_device(0, planes.data_ptr(), planes.numel() * 8, st)
+    sh.copy_from_device(0, scales.data_ptr(), scales.numel() * 2, st)
+    torch.cuda.synchronize()
+    pl = F.plan(dev(qs), dev(lam), w.budget, 0, rot=dev(rot))
+    ref = F.scan_topk(planes, scales, n, pl, k)
+    got = F.scan_topk(ph.dev, sh.dev, n, pl, k)
+    staged = F.TopkOut(P, w.G, n, k, pl.q_used.device, fused=True)
+    for stage in (1, 2, 3):
+        F.scan_topk_stage(stage, ph.dev, sh.dev, n, pl, staged)
+    s_host = F.scan(ph.dev, sh.dev, n, pl)
+    torch.cuda.synchronize()
+    for o in (got, staged):
+        assert torch.equal(ref.idx, o.idx) and torch.equal(ref.val, o.val)
+        assert torch.equal(ref.union, o.union) and torch.equal(ref.union_len, o.union_len)
+    _compare_pair(orc, 0, xs[0], qs[0], lam[0], w.budget, k, n, pl, s_host, got, rot=rot[0], keys_rot=rot[0])
+    ph.free()
+    sh.free()
+
+
 @pytest.mark.parametrize("shared,host", [(False, False), (True, False), (False, True), (True, True)])
 def test_gather_rows_bit_exact(F, orc, shared, host):
     """Winner-row fetch: union rows of every pair copied out of a K|V row
