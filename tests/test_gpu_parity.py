@@ -555,15 +555,16 @@ def test_host_resident_index_matches_device(F, orc):
     sh.free()
 
 
-@pytest.mark.parametrize("k", [64, 512])
-def test_host_resident_staged_sample(F, orc, k):
+@pytest.mark.parametrize("k,mode,budget", [(64, 0, 48), (512, 0, 48), (512, 1, 32)])
+def test_host_resident_staged_sample(F, orc, k, mode, budget):
     """Over the host link the sample stage keeps its scores and the filter
     skips the sampled runs (every index byte read once).  At n = 600,013 the
     sample is one run in 32 for k = 64 (group maxima set the threshold, the
     scores are stored beside them) and one run in 16 for k = 512 (every
-    sampled score, which are also the stored ones).  One call, the three stages
-    called one by one, and the same step from HBM must all give the same
-    winners, values and unions, equal to the oracle's."""
+    sampled score, which are also the stored ones).  The 136-bit fixed plan
+    (mode 1, r = 32) takes the slot-shared scan form.  One call, the three
+    stages called one by one, and the same step from HBM must all give the
+    same winners, values and unions, equal to the oracle's."""
     import torch
 
     from sparse_attention_key_amd.hostmem import PinnedHost
@@ -576,7 +577,7 @@ def test_host_resident_staged_sample(F, orc, k):
     qs = np.stack([wl.queries(w, p) for p in range(P)])
     rots, lams = zip(*[orc.calib.klt_basis(wl.calibration_sample(w, p)) for p in range(P)])
     rot, lam = np.stack(rots), np.stack(lams)
-    say("host-resident staged sample", n, k)
+    say("host-resident staged sample", n, k, mode, budget)
     planes, scales = F.pack(bf16_dev(np.stack(xs)), rot=dev(rot))
     ph = PinnedHost(planes.numel() * 8)
     sh = PinnedHost(scales.numel() * 2)
@@ -584,7 +585,7 @@ def test_host_resident_staged_sample(F, orc, k):
     ph.copy_from_device(0, planes.data_ptr(), planes.numel() * 8, st)
     sh.copy_from_device(0, scales.data_ptr(), scales.numel() * 2, st)
     torch.cuda.synchronize()
-    pl = F.plan(dev(qs), dev(lam), w.budget, 0, rot=dev(rot))
+    pl = F.plan(dev(qs), dev(lam), budget, mode, rot=dev(rot))
     ref = F.scan_topk(planes, scales, n, pl, k)
     got = F.scan_topk(ph.dev, sh.dev, n, pl, k)
     staged = F.TopkOut(P, w.G, n, k, pl.q_used.device, fused=True)
@@ -595,7 +596,8 @@ def test_host_resident_staged_sample(F, orc, k):
     for o in (got, staged):
         assert torch.equal(ref.idx, o.idx) and torch.equal(ref.val, o.val)
         assert torch.equal(ref.union, o.union) and torch.equal(ref.union_len, o.union_len)
-    _compare_pair(orc, 0, xs[0], qs[0], lam[0], w.budget, k, n, pl, s_host, got, rot=rot[0], keys_rot=rot[0])
+    _compare_pair(orc, 0, xs[0], qs[0], lam[0], budget, k, n, pl, s_host, got, mode=mode, rot=rot[0],
+                  keys_rot=rot[0])
     ph.free()
     sh.free()
 
