@@ -2,8 +2,9 @@
 workspace is the library's fixed per-GPU scratch), against fathom_scan_topk
 with a workspace of its own: the same kernels run, so every output must be
 the same bits.  Calls follow one another on the one scratch: a large one, a
-smaller one after it (the scratch keeps the first call's contents), and one
-whose every pair needs the repair rows."""
+smaller one after it (the scratch keeps the first call's contents), one
+whose every pair needs the repair rows, and one over an index in host
+memory (the staged sample in the scratch)."""
 import numpy as np
 import pytest
 import torch
@@ -63,6 +64,33 @@ def test_noalloc_repairs_failed_pairs_in_the_scratch(F):
     _check_same(F, planes, scales, 3000 + 5, pl, 100)
     planes, scales, pl = _inputs(F, 5, 777, 4, 128, 48, 4)
     _check_same(F, planes, scales, 777, pl, 50)
+
+
+def test_noalloc_reads_a_host_index_once(F):
+    """An index in mapped pinned host memory takes the staged sample (the
+    sample's scores kept in the scratch, the filter skipping the sampled
+    runs); the outputs equal the workspace entry point's on the same index
+    in device memory."""
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    P, n, k = 4, 300000 + 13, 512
+    say("no-alloc fused scan + top-k, index in host memory", P, n, k)
+    planes, scales, pl = _inputs(F, P, n, 4, 128, 48, 5)
+    ph = PinnedHost(planes.numel() * 8)
+    sh = PinnedHost(scales.numel() * 2)
+    st = torch.cuda.current_stream()
+    ph.copy_from_device(0, planes.data_ptr(), planes.numel() * 8, st)
+    sh.copy_from_device(0, scales.data_ptr(), scales.numel() * 2, st)
+    torch.cuda.synchronize()
+    ref = F.scan_topk(planes, scales, n, pl, k)
+    got = F.TopkOut(P, 4, n, k, "cuda", workspace=False)
+    F.scan_topk_noalloc_into(ph.dev, sh.dev, n, pl, got)
+    torch.cuda.synchronize()
+    assert torch.equal(got.idx, ref.idx)
+    assert torch.equal(got.val.view(torch.int32), ref.val.view(torch.int32))
+    assert torch.equal(got.union_len, ref.union_len) and torch.equal(got.union, ref.union)
+    ph.free()
+    sh.free()
 
 
 def test_noalloc_rejects_a_call_larger_than_the_scratch(F):
