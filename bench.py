@@ -63,17 +63,18 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
-def sample_fraction(n: int, k: int) -> float:
+def sample_fraction(n: int, k: int, run: int = 32) -> float:
     """Share of the index blocks in the fused threshold's sample: one run of
-    32 blocks in every s runs, s the largest power of two with (2s)^2 4k <= n
-    and 2s <= the block count (the library's rule).  Over the host link the
-    sample stage reads these blocks and the filter the rest."""
+    `run` blocks (32, or 512 for an index read over the host link) in every
+    s runs, s the largest power of two with (2s)^2 4k <= n and 2s <= the
+    block count (the library's rule).  Over the host link the sample stage
+    reads these blocks and the filter the rest."""
     nb = (n + 63) // 64
     s = 1
     while (2 * s) ** 2 * 4 * k <= n and 2 * s <= nb:
         s *= 2
-    runs = (nb + 31) // 32
-    sampled = sum(min(32, nb - r * 32) for r in range(0, runs, s))
+    runs = (nb + run - 1) // run
+    sampled = sum(min(run, nb - r * run) for r in range(0, runs, s))
     return sampled / nb
 
 
@@ -583,7 +584,7 @@ def main():
         # runs and the filter every other block, each once; their own rates
         # are reported beside the fraction.)
         peak = max(link["zero_copy_read"], link["pinned_h2d_memcpy"])
-        fs = sample_fraction(w.n, w.k)
+        fs = sample_fraction(w.n, w.k, run=512)
         step_gbs = alg_bytes / (gpu_ms * 1e-3) / 1e9
         roof = {"bound": "host_link", "kernel": "whole step (plan, sample, filtered scan, select)",
                 "achieved": round(step_gbs, 2), "peak": peak,

@@ -127,6 +127,7 @@ struct ScanArgs {
     int64_t stride;        // 1, or: scan one run of 32 consecutive blocks in every stride runs
     int64_t skip;          // 0, or a power of two s >= 2: the runs the sample took (one in every s,
                            // the first included) are neither read nor filtered
+    int run_log2;          // sampled runs are 2^run_log2 blocks long (0: 32 blocks)
     int64_t nlb;           // logical blocks per pair (rows of the STORE output / 64)
     float* out;            // STORE: [P][G][nlb * 64]; LANEMAX: [P][G][nlb * 4] (maxima of 16 tokens)
     float* out2;           // LANEMAX, or null: every score as well ([P][G][nlb * 64], as STORE)
@@ -161,6 +162,7 @@ struct TopkLayout {
     bool lanemax;        // fused threshold from per-lane maxima of the sample
     bool staged;         // fused: the sample stores every score it reads, and stage 2 filters
                          // those stored scores instead of reading the sampled runs again
+    int run_log2;        // the sample's runs are 2^run_log2 blocks long
     int rank;            // fused threshold: this order statistic of the sample
     size_t off_tau, off_count, off_cand, off_sorted, bytes;  // top-k from given scores
     int slots;           // fused: full score rows (pairs) for the repair, reused in turn

@@ -53,7 +53,7 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kGroupBlocks = 1024;                 // logical blocks per workgroup (at most)
-constexpr int kRun = 32;                           // sampled blocks come in runs of 32
+constexpr int kRunLog2 = 5;                        // sampled blocks come in runs of 32 (unless set)
 constexpr int kSlotsMax = 128;
 constexpr int kRec = 32;                           // LDS bytes per (slot, half block) code record
 constexpr int kCodeBytes = 8 * 32 * kRec + 8 * 32;   // 2 (4/C) half blocks of 32 C slots and a spare record
@@ -369,12 +369,15 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const int p, const 
 #pragma unroll
     for (int r = 0; r < 4; ++r) arow[r] = (uint32_t)(((32 * r + 8 * kap + (j16 >> 1)) * 2 + (j16 & 1)) * 8);
 
-    // physical block of a logical one: runs of kRun, one run in every stride.
+    // physical block of a logical one: runs of 2^rlog blocks, one run in every stride.
     // The NB blocks of an iteration lie in one run, so they are consecutive;
     // blocks past the index read as zeros (the buffer bound) and are masked.
-    auto phys = [&](int lb) { return __builtin_amdgcn_readfirstlane((lb / kRun) * kRun * stride + (lb % kRun)); };
+    const int rlog = a.run_log2 ? a.run_log2 : kRunLog2;
+    auto phys = [&](int lb) {
+        return __builtin_amdgcn_readfirstlane(((lb >> rlog) * stride << rlog) + (lb & ((1 << rlog) - 1)));
+    };
     // a physical block in a run that the sample stage took (staged filter: not read, no candidates)
-    auto sampled = [&](int pb) { return STG && MODE == kFilter && ((pb / kRun) & (skip - 1)) == 0; };
+    auto sampled = [&](int pb) { return STG && MODE == kFilter && ((pb >> rlog) & (skip - 1)) == 0; };
     // per-lane offset of plane s of step u; a plane the slot does not read
     // gets bit 31 set, which is out of range (kept in vector registers: a
     // per-plane lane mask would take scalar registers for the whole loop)
@@ -851,12 +854,15 @@ __device__ __forceinline__ void scan_body_shared(const ScanArgs& a, const int p,
 #pragma unroll
     for (int r = 0; r < 4; ++r) arow[r] = (uint32_t)(((32 * r + 8 * kap + (j16 >> 1)) * 2 + (j16 & 1)) * 8);
 
-    // physical block of a logical one: runs of kRun, one run in every stride.
+    // physical block of a logical one: runs of 2^rlog blocks, one run in every stride.
     // The NB blocks of an iteration lie in one run, so they are consecutive;
     // blocks past the index read as zeros (the buffer bound) and are masked.
-    auto phys = [&](int lb) { return __builtin_amdgcn_readfirstlane((lb / kRun) * kRun * stride + (lb % kRun)); };
+    const int rlog = a.run_log2 ? a.run_log2 : kRunLog2;
+    auto phys = [&](int lb) {
+        return __builtin_amdgcn_readfirstlane(((lb >> rlog) * stride << rlog) + (lb & ((1 << rlog) - 1)));
+    };
     // a physical block in a run that the sample stage took (staged filter: not read, no candidates)
-    auto sampled = [&](int pb) { return STG && MODE == kFilter && ((pb / kRun) & (skip - 1)) == 0; };
+    auto sampled = [&](int pb) { return STG && MODE == kFilter && ((pb >> rlog) & (skip - 1)) == 0; };
     // per-lane offset of plane s of the lane's row segment; a plane the slot
     // does not read gets bit 31 set, which is out of range (kept in vector
     // registers: a per-plane lane mask would take scalar registers for the
@@ -1366,26 +1372,47 @@ hipError_t launch_mode(const ScanArgs& args, int P, int G, hipStream_t st)
     ScanArgs a = args;
     const int rows = P;
     // blocks per workgroup: 1024, or fewer (a multiple of every iteration's
-    // 16 blocks, at least 64, or 32 for the staged sample) while the grid has fewer workgroups than
+    // 16 blocks, at least 64; see below for few pairs and the staged sample)
+    // while the grid has fewer workgroups than
     // `target`.  Long ranges spread each workgroup's start-up (the pair's
     // tables, the first loads, the last flush) over more blocks: at 1M
     // tokens x 288 pairs the filtered scan takes 1.10 ms with 256 blocks per
     // workgroup, 0.98 with 512, 0.96 with 1024 and 1.00 with 2048.  For the
-    // full scans (filter, scores) of few pairs a grid of about two
-    // workgroups per CU is best: at 1M tokens x 8 pairs (one layer) the
-    // filter takes 110 us with 2048 workgroups of 64 blocks, 77 with 1024,
-    // 56 with 512 and 64 with 256.  Many pairs of shorter rows want the
+    // full scans of few pairs a grid of about two workgroups per CU does
+    // well: at 1M tokens x 8 pairs (one layer) the filter takes 110 us with
+    // 2048 workgroups of 64 blocks, 77 with 1024, 56 with 512 and 64 with
+    // 256 (and 54.7 with the 632 of 208 blocks the rule below picks; 60.8
+    // with 552, 57.3 with 752).  Many pairs of shorter rows want the
     // larger grid: at 131k tokens x 288 pairs 2304 workgroups of 256 blocks
     // filter in 0.19 ms against 0.22 for 576 of 1024.  The sampled stage
     // reads one run in 16, so its workgroups are short and more of them
     // (2048) keep the chip busy: 0.105 ms at 288 pairs against 0.125 with 512.
-    // The staged sample of an index read over the host link (a.out2 set)
-    // wants the shortest workgroups, 32 blocks: 3.95 ms at 1M tokens x 288
-    // pairs against 4.08 with 64, 4.25 with 256 and 4.42 with 128.
+    // The staged sample of an index read over the host link (a.out2 set,
+    // runs of 512 blocks) wants about 512 long workgroups, down to 32
+    // blocks for few pairs: at 1M tokens x 288 pairs 3.67 ms with 576 of
+    // 512 blocks against 3.83 with 32-block ones (and 3.97 for runs of 32).
+    // Calls of few pairs (a layer's 8 KV heads) are latency-bound: a
+    // workgroup's start-up (tables, first loads, last flush) costs about as
+    // much as several iterations, so their grids aim at one round of
+    // workgroups.  The sampled stage may go down to 16-block (one-iteration)
+    // workgroups; the filter takes about 640 workgroups (2.5 per CU), or one
+    // per CU where that would leave fewer than 64 blocks each.  One layer at
+    // 1M tokens: sample 27 -> 23 us, filter 56.5 -> 54.7 us; the 36-layer
+    // step 4.18 -> 3.96 ms, at 131k 3.47 -> 3.27 ms, the 32k step 95 -> 83 us.
+    // Over the host link (the staged filter, a.skip set) longer workgroups
+    // read faster, so that filter keeps the halving rule (36 layers at 1M:
+    // 55.0 ms against 57.0 with the few-pairs grid).
     const bool host_sample = MODE == kLaneMax && a.out2 != nullptr;
-    const int64_t target = host_sample ? 8192 : MODE == kLaneMax || rows >= 64 ? 2048 : 512;
+    const int64_t target = host_sample ? 512 : MODE == kLaneMax || rows >= 64 ? 2048 : 512;
+    const int floor_gb = host_sample ? 32 : (MODE == kLaneMax || (MODE == kStore && rows < 64)) ? 16 : 64;
     a.gb = kGroupBlocks;
-    while (a.gb > (host_sample ? 32 : 64) && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < target) a.gb /= 2;
+    while (a.gb > floor_gb && (int64_t)((a.nlb + a.gb - 1) / a.gb) * rows < target) a.gb /= 2;
+    if (MODE == kFilter && rows < 64 && a.skip == 0) {
+        const int64_t work = a.nlb * rows;
+        int64_t g = ((work + 639) / 640 + 15) / 16 * 16;
+        if (g < 64) g = ((work + 255) / 256 + 15) / 16 * 16;
+        a.gb = (int)(g < 16 ? 16 : g > kGroupBlocks ? kGroupBlocks : g);
+    }
     dim3 grid((unsigned)((a.nlb + a.gb - 1) / a.gb), (unsigned)rows);
     const bool stg = (MODE == kFilter && a.skip != 0) || (MODE == kLaneMax && a.out2 != nullptr);
     if (MODE != kStore && stg) {
