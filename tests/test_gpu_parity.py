@@ -602,6 +602,44 @@ def test_host_resident_staged_sample(F, orc, k, mode, budget):
     sh.free()
 
 
+def test_host_resident_small_workspace_falls_back(F):
+    """A workspace large enough for the device layout but not for the staged
+    sample (here 40 pairs at 65,536 tokens, k = 64: the stored sample scores,
+    one 512-block run per pair, take 20 MiB against the 16 MiB of repair rows
+    they share memory with) still gives the same results over the host link,
+    without the staging."""
+    from sparse_attention_key_amd.hostmem import PinnedHost
+
+    P, G, D, n, k = 40, 4, 128, 65536, 64
+    g = np.random.default_rng(515)
+    x = (g.standard_normal((P, n, D)) * np.exp(0.7 * g.standard_normal((P, 1, D)))).astype(np.float32)
+    q, s2 = _plan_inputs(P, G, D, 516)
+    say("host-resident index, workspace below the staged layout", P, n, k)
+    planes, scales = F.pack(dev(x))
+    del x
+    ph = PinnedHost(planes.numel() * 8)
+    sh = PinnedHost(scales.numel() * 2)
+    st = torch.cuda.current_stream()
+    ph.copy_from_device(0, planes.data_ptr(), planes.numel() * 8, st)
+    sh.copy_from_device(0, scales.data_ptr(), scales.numel() * 2, st)
+    torch.cuda.synchronize()
+    pl = F.plan(dev(q), dev(s2), 48, 0)
+    ref = F.scan_topk(planes, scales, n, pl, k)
+    full = F.scan_topk_workspace_bytes(P, G, n, k)
+    outs = []
+    for ws_bytes in (full, full - (512 << 10)):
+        o = F.TopkOut(P, G, n, k, pl.q_used.device, fused=True)
+        o.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=pl.q_used.device)
+        F.scan_topk_into(ph.dev, sh.dev, n, pl, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(ref.idx, o.idx) and torch.equal(ref.val, o.val)
+        assert torch.equal(ref.union, o.union) and torch.equal(ref.union_len, o.union_len)
+    ph.free()
+    sh.free()
+
+
 @pytest.mark.parametrize("shared,host", [(False, False), (True, False), (False, True), (True, True)])
 def test_gather_rows_bit_exact(F, orc, shared, host):
     """Winner-row fetch: union rows of every pair copied out of a K|V row
